@@ -1,0 +1,191 @@
+/*
+ * mla_paged_kv.h -- C ABI of the MI355X (gfx950) MLA decode library.
+ *
+ * Multi-head latent attention decode over a paged KV cache: for every query
+ * row (request r, new token i, head h)
+ *
+ *     out = softmax(scale * q . K^T) . V,   lse = log(sum_j exp(scale * q . k_j))
+ *
+ * where all h_q heads share one latent KV head of 576 dims (512 "NoPE" dims
+ * followed by 64 RoPE dims) and V is its first 512 dims.  This is the dense MLA
+ * decode of "Add SM80 (Ampere/A100) dense MLA decode kernel" (FlashMLA pull
+ * request 183: Summary -- dense decode entry point plus combine kernel;
+ * Design -- 576-dim Q/K, 512 V columns; Test plan -- causal multi-token
+ * queries, split-K via the combine), and the packed top-k FP8 variant of
+ * "[SM90] Add packed selected-KV sparse decode" (FlashMLA pull request 200:
+ * "SM90 packing kernel", "Packed attention specialization", "Python API",
+ * "Supported scope").
+ *
+ * Conventions for every call below:
+ *   - Pointers marked (device) are device pointers on the current HIP device;
+ *     the library dereferences none of them on the host.  `stream` is a
+ *     hipStream_t (NULL = the default stream); every device-side call is
+ *     asynchronous on it.
+ *   - The caller allocates and owns every buffer.  The library allocates no
+ *     device memory, keeps no per-call state and keeps no pointer after a call
+ *     returns.  Inputs are only read.
+ *   - Every call returns an mla_status.  Arguments outside the supported scope
+ *     are rejected with MLA_ERR_UNSUPPORTED before anything is launched; bad
+ *     pointers or sizes give MLA_ERR_INVALID_ARGUMENT or
+ *     MLA_ERR_WORKSPACE_TOO_SMALL; a failed HIP call gives MLA_ERR_HIP.
+ *     mla_last_error_message() describes the last failure on this thread.
+ *   - Data-dependent preconditions (checking them would need a device sync)
+ *     are the caller's contract: 0 <= seqlens[r] <= max_pages * 64, page ids of
+ *     used blocks in [0, num_pages), top-k ids of the valid prefix in
+ *     [0, num_pages * 64).  The kernels bounds-check them anyway, never read
+ *     out of range, and record a violation in a device flag that
+ *     mla_read_device_errors() returns.
+ *
+ * Layouts (all row-major, contiguous):
+ *   q            bf16  [batch][s_q][h_q][576]
+ *   kcache       bf16  [num_pages][64][1][576]           (MLA_KV_BF16_PAGED)
+ *   kcache_fp8   uint8 [num_pages][64][1][656]           656-byte records:
+ *                  bytes [0,512) E4M3FN NoPE, [512,528) 4 x fp32 LE scales
+ *                  (scale k covers NoPE dims [128k, 128k+128)), [528,656)
+ *                  64 x bf16 LE RoPE.  Key = (e4m3 * scale, rope).
+ *   block_table  int32 [batch][max_pages]   page id of each 64-token block
+ *   seqlens      int32 [batch]   cached tokens per request, including the s_q
+ *                                new ones; the s_q new tokens are the last s_q
+ *                                positions (causal mask is bottom-right: token
+ *                                i sees keys [0, seqlen - s_q + i])
+ *   out          bf16  [batch][s_q][h_q][512]
+ *   lse          fp32  [batch][s_q][h_q]   natural log; -inf for a row with no
+ *                                          visible key (its out is 0)
+ *   sched_meta   int32 [num_parts][8]      (see mla_get_decode_metadata)
+ *   num_splits   int32 [batch + 1]         exclusive prefix sum of splits
+ */
+#ifndef MLA_PAGED_KV_H
+#define MLA_PAGED_KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_D_QK 576
+#define MLA_D_V 512
+#define MLA_PAGE_TOKENS 64
+#define MLA_FP8_RECORD_BYTES 656
+#define MLA_SCHED_META_INTS 8
+#define MLA_MAX_ROWS 256       /* s_q * h_q per request */
+#define MLA_MAX_BATCH 65536
+#define MLA_MAX_PARTS 8192
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARGUMENT = -1,
+  MLA_ERR_UNSUPPORTED = -2,
+  MLA_ERR_WORKSPACE_TOO_SMALL = -3,
+  MLA_ERR_HIP = -4
+} mla_status;
+
+typedef enum {
+  MLA_KV_BF16_PAGED = 0, /* kcache bf16 pages reached through block_table */
+  MLA_KV_FP8_PACKED = 1  /* the workspace written by mla_pack_selected_kv */
+} mla_kv_format;
+
+/* Text of the last error on the calling host thread ("" if none).  The
+ * pointer stays valid until the next library call on that thread. */
+const char* mla_last_error_message(void);
+
+/* Recommended split count (partitions of the KV work) for a decode launch on
+ * the current device: workgroups that fit per CU (from the compiled kernel's
+ * LDS and register footprint, via the HIP occupancy query) times the CU
+ * count, divided by the row blocks per request, then capped so that no
+ * request is cut into more pieces than an empirical limit (the partition count
+ * is scaled to resident workgroups rather than to the CU count, and gated by
+ * measured limits: "How the occupancy work went", FlashMLA PR 183).  Host
+ * only; queries the device. */
+int mla_decode_num_parts(int batch, int s_q, int h_q, int h_kv, int kv_format, int* num_parts_out);
+
+/* The same policy as a pure function of the device figures (for tests and for
+ * callers planning for another device): cus = compute units, wgs_per_cu =
+ * decode workgroups resident per CU. */
+int mla_plan_num_parts(int batch, int s_q, int h_q, int kv_format, int cus, int wgs_per_cu, int* num_parts_out);
+
+/* Bytes of the caller-owned decode workspace (split partials: fp32 partial
+ * outputs and lse for at most batch + num_parts splits).  0 on bad input. */
+size_t mla_decode_workspace_size(int batch, int s_q, int h_q, int num_parts);
+
+/* Bytes of the packed top-k workspace: batch * s_q * topk_capacity * 656
+ * (one 656-byte record per selected slot; 2048 slots = 1,343,488 B per query
+ * row -- "Runtime follow-up", FlashMLA PR 200).  0 on bad input. */
+size_t mla_packed_kv_workspace_size(int batch, int s_q, int topk_capacity);
+
+/* Scheduler metadata (device, one workgroup).  Splits the KV blocks of all
+ * requests into num_parts contiguous partitions.  Definition: request r has
+ * ceil(seqlens[r] / 64) blocks (seqlens = topk_length for the packed path),
+ * T blocks in total, and P' = min(num_parts, T); concatenating all requests'
+ * blocks in order, partition p < P' owns global blocks
+ * [floor(p*T/P'), floor((p+1)*T/P')) -- at least one -- and partitions
+ * p >= P' own none.
+ *   sched_meta[p] = { begin_req, begin_block, end_req, end_block_exclusive,
+ *                     split index of the first piece within begin_req, 0, 0, 0 }
+ *                   or { -1, -1, -1, -1, -1, 0, 0, 0 } for an empty partition;
+ *   num_splits[0] = 0, num_splits[r+1] = num_splits[r] + (partitions owning a
+ *                   block of request r).
+ * seqlens (device) [batch]; sched_meta (device) [num_parts][8]; num_splits
+ * (device) [batch + 1].  Call once per decode step; reuse across layers. */
+int mla_get_decode_metadata(const int32_t* seqlens, int batch, int s_q, int h_q, int h_kv, int num_parts,
+                            int32_t* sched_meta, int32_t* num_splits, void* stream);
+
+/* Decode (device).  Launches num_parts x ceil(s_q*h_q / 128) workgroups; each
+ * walks its partition's pages with an online softmax and writes either the
+ * final out/lse rows (request not split) or a split partial into `workspace`.
+ * mla_combine must follow on the same stream to finish split requests.
+ *   q (device) bf16 [batch][s_q][h_q][576]
+ *   kv (device): MLA_KV_BF16_PAGED -> kcache bf16 [num_pages][64][1][576];
+ *                MLA_KV_FP8_PACKED -> packed workspace of mla_pack_selected_kv
+ *                (then block_table/max_pages/num_pages are ignored, seqlens is
+ *                topk_length, s_q must be 1, h_q must be 64 or 128, no causal)
+ *   block_table (device) int32 [batch][max_pages], seqlens (device) int32 [batch]
+ *   softmax_scale: multiplies q.k (e.g. 576^-0.5); causal: 0/1
+ *   sched_meta, num_splits (device): from mla_get_decode_metadata with the same
+ *     seqlens, batch and num_parts
+ *   out (device) bf16 [batch][s_q][h_q][512], lse (device) fp32 [batch][s_q][h_q]
+ *   workspace (device) of >= mla_decode_workspace_size(batch, s_q, h_q, num_parts)
+ * Scope: h_kv = 1; h_q a multiple of 16 with h_q <= 128; s_q * h_q <= 256;
+ * gfx950 device. */
+int mla_decode_fwd(const void* q, const void* kv, int kv_format, int64_t num_pages, const int32_t* block_table,
+                   int max_pages, const int32_t* seqlens, int topk_capacity, int batch, int s_q, int h_q, int h_kv,
+                   float softmax_scale, int causal, const int32_t* sched_meta, const int32_t* num_splits,
+                   int num_parts, void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Combine (device): for every request with >= 2 splits, merges its partials
+ * from `workspace` by log-sum-exp, L = log(sum_i exp(lse_i)),
+ * out = sum_i exp(lse_i - L) * o_i, lse = L (a split with lse -inf has weight
+ * 0); a request with 0 splits (no key) gets out = 0, lse = -inf; a request with
+ * one split was finished by mla_decode_fwd and is left untouched.  The split
+ * count is a runtime value; there is no fixed ladder of supported counts. */
+int mla_combine(const int32_t* num_splits, const void* workspace, size_t workspace_bytes, int batch, int s_q,
+                int h_q, int num_parts, void* out, float* lse, void* stream);
+
+/* Pack (device): copies the selected 656-byte records byte-for-byte into the
+ * tile-major workspace ws[row][tile][slot][656], row = r * s_q + i,
+ * tile = k / 64, slot = k % 64, for k < topk_length[r] the record of physical
+ * token indices[r][i][k] (page = id / 64, slot = id % 64); slots
+ * k >= topk_length[r] are zero-filled.  Tile t of a row is byte-identical to a
+ * pool page holding that row's selected records k = 64t .. 64t+63 in order.
+ *   kcache_fp8 (device) uint8 [num_pages][64][1][656]; indices (device) int32
+ *   [batch][s_q][topk_capacity]; topk_length (device) int32 [batch];
+ *   workspace (device) >= mla_packed_kv_workspace_size(batch, s_q, topk_capacity).
+ * Scope: topk_capacity a positive multiple of 64. */
+int mla_pack_selected_kv(const void* kcache_fp8, int64_t num_pages, const int32_t* indices,
+                         const int32_t* topk_length, int batch, int s_q, int topk_capacity, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Device-side violation flags accumulated by the kernels on the current
+ * device since the last call (bit 0: page id out of range, bit 1: top-k id
+ * out of range, bit 2: seqlen above max_pages * 64 or top-k length above the
+ * capacity, bit 3: sched_meta / num_splits not produced by
+ * mla_get_decode_metadata for this batch and num_parts).  Synchronises `stream`
+ * and clears the flags. */
+int mla_read_device_errors(int* flags_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_PAGED_KV_H */

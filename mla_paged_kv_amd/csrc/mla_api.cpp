@@ -1,0 +1,260 @@
+// C ABI of the MLA decode library (declarations and contracts: include/mla_paged_kv.h).
+//
+// Host side only: argument validation (fail closed before any launch, as the
+// packed path's "Supported scope" on FlashMLA PR 200 asks of unsupported
+// shapes), the occupancy-derived split count (FlashMLA PR 183, "How the
+// occupancy work went"), workspace sizing and kernel dispatch.
+#include "../../include/mla_paged_kv.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+
+#include "mla_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return MLA_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Empirical partition gate: at most this many pieces per request.  Each extra
+// piece re-reads the request's Q rows, runs a prologue/epilogue and writes a
+// 128 x 513 fp32 partial that the combine re-reads, so splitting finer than
+// the occupancy needs costs bandwidth.  EMPIRICAL: an initial value, not
+// derived; it is meant to be re-read off an MI355X sweep of the decode kernel.
+constexpr int kMaxSplitsPerRequest = 16;
+
+bool is_gfx950() {
+  static int cache[64];  // 0 unknown, 1 gfx950, 2 other (benign race: same value written)
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (dev >= 0 && dev < 64 && cache[dev]) return cache[dev] == 1;
+  hipDeviceProp_t p;
+  if (hipGetDeviceProperties(&p, dev) != hipSuccess) return false;
+  const bool yes = strncmp(p.gcnArchName, "gfx950", 6) == 0;
+  if (dev >= 0 && dev < 64) cache[dev] = yes ? 1 : 2;
+  return yes;
+}
+
+int check_device() {
+  int n = 0;
+  hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess || n == 0) return fail(MLA_ERR_HIP, "no HIP device: %s", hipGetErrorString(e));
+  if (!is_gfx950()) return fail(MLA_ERR_UNSUPPORTED, "device is not gfx950 (MI355X)");
+  return MLA_OK;
+}
+
+// Scope checks shared by the decode entry points.
+int check_shape(int batch, int s_q, int h_q, int h_kv, int kv_format) {
+  if (batch < 1 || batch > MLA_MAX_BATCH) return fail(MLA_ERR_INVALID_ARGUMENT, "batch %d out of [1, %d]", batch, MLA_MAX_BATCH);
+  if (batch > mla::kSchedMaxBatch)
+    return fail(MLA_ERR_UNSUPPORTED, "batch %d above the scheduler limit %d", batch, mla::kSchedMaxBatch);
+  if (s_q < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "s_q %d < 1", s_q);
+  if (h_q < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "h_q %d < 1", h_q);
+  if (h_kv != 1) return fail(MLA_ERR_UNSUPPORTED, "h_kv %d: only one latent KV head is supported", h_kv);
+  if (h_q % 16 != 0 || h_q > 128) return fail(MLA_ERR_UNSUPPORTED, "h_q %d: must be a multiple of 16 and <= 128", h_q);
+  if ((int64_t)s_q * h_q > MLA_MAX_ROWS) return fail(MLA_ERR_UNSUPPORTED, "s_q * h_q = %d above %d", s_q * h_q, MLA_MAX_ROWS);
+  if (kv_format != MLA_KV_BF16_PAGED && kv_format != MLA_KV_FP8_PACKED)
+    return fail(MLA_ERR_UNSUPPORTED, "kv_format %d unknown", kv_format);
+  if (kv_format == MLA_KV_FP8_PACKED) {
+    if (s_q != 1) return fail(MLA_ERR_UNSUPPORTED, "packed FP8 decode supports s_q = 1 only (got %d)", s_q);
+    if (h_q != 64 && h_q != 128) return fail(MLA_ERR_UNSUPPORTED, "packed FP8 decode supports h_q in {64, 128} (got %d)", h_q);
+  }
+  return MLA_OK;
+}
+
+int slots_for(int batch, int num_parts) { return batch + num_parts; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_last_error_message(void) { return g_last_error.c_str(); }
+
+int mla_plan_num_parts(int batch, int s_q, int h_q, int kv_format, int cus, int wgs_per_cu, int* num_parts_out) {
+  if (!num_parts_out) return fail(MLA_ERR_INVALID_ARGUMENT, "num_parts_out is NULL");
+  int st = check_shape(batch, s_q, h_q, 1, kv_format);
+  if (st) return st;
+  if (cus < 1 || wgs_per_cu < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "cus %d / wgs_per_cu %d must be >= 1", cus, wgs_per_cu);
+  const int M = s_q * h_q;
+  const int rb = 16 * mla::decode_row_blocks_per_wg(M);
+  const int row_blocks = (M + rb - 1) / rb;
+  int64_t slots = (int64_t)cus * wgs_per_cu;
+  int64_t parts = slots / row_blocks;
+  if (parts < 1) parts = 1;
+  const int64_t cap = (int64_t)batch * kMaxSplitsPerRequest;
+  if (parts > cap) parts = cap;
+  if (parts > MLA_MAX_PARTS) parts = MLA_MAX_PARTS;
+  *num_parts_out = (int)parts;
+  return ok();
+}
+
+int mla_decode_num_parts(int batch, int s_q, int h_q, int h_kv, int kv_format, int* num_parts_out) {
+  if (!num_parts_out) return fail(MLA_ERR_INVALID_ARGUMENT, "num_parts_out is NULL");
+  int st = check_shape(batch, s_q, h_q, h_kv, kv_format);
+  if (st) return st;
+  st = check_device();
+  if (st) return st;
+  int dev = 0, cus = 0, wgs = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "device query");
+  e = mla::decode_occupancy(kv_format == MLA_KV_FP8_PACKED, s_q * h_q, &wgs);
+  if (e != hipSuccess) return hip_fail(e, "occupancy query");
+  if (wgs < 1) return fail(MLA_ERR_HIP, "decode kernel does not fit on a CU");
+  return mla_plan_num_parts(batch, s_q, h_q, kv_format, cus, wgs, num_parts_out);
+}
+
+size_t mla_decode_workspace_size(int batch, int s_q, int h_q, int num_parts) {
+  if (batch < 1 || s_q < 1 || h_q < 1 || num_parts < 1 || num_parts > MLA_MAX_PARTS || batch > MLA_MAX_BATCH) return 0;
+  const size_t M = (size_t)s_q * h_q;
+  return (size_t)slots_for(batch, num_parts) * M * (mla::kDV + 1) * sizeof(float);
+}
+
+size_t mla_packed_kv_workspace_size(int batch, int s_q, int topk_capacity) {
+  if (batch < 1 || s_q < 1 || topk_capacity < 1 || topk_capacity % mla::kPage != 0) return 0;
+  return (size_t)batch * s_q * topk_capacity * mla::kRecBytes;
+}
+
+int mla_get_decode_metadata(const int32_t* seqlens, int batch, int s_q, int h_q, int h_kv, int num_parts,
+                            int32_t* sched_meta, int32_t* num_splits, void* stream) {
+  if (!seqlens || !sched_meta || !num_splits) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (num_parts < 1 || num_parts > MLA_MAX_PARTS)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "num_parts %d out of [1, %d]", num_parts, MLA_MAX_PARTS);
+  int st = check_shape(batch, s_q, h_q, h_kv, MLA_KV_BF16_PAGED);
+  if (st) return st;
+  st = check_device();
+  if (st) return st;
+  hipError_t e = mla::launch_sched(seqlens, batch, num_parts, sched_meta, num_splits, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "scheduler launch");
+  return ok();
+}
+
+int mla_decode_fwd(const void* q, const void* kv, int kv_format, int64_t num_pages, const int32_t* block_table,
+                   int max_pages, const int32_t* seqlens, int topk_capacity, int batch, int s_q, int h_q, int h_kv,
+                   float softmax_scale, int causal, const int32_t* sched_meta, const int32_t* num_splits,
+                   int num_parts, void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !kv || !seqlens || !sched_meta || !num_splits || !out || !lse)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  int st = check_shape(batch, s_q, h_q, h_kv, kv_format);
+  if (st) return st;
+  const bool fp8 = kv_format == MLA_KV_FP8_PACKED;
+  if (fp8) {
+    if (topk_capacity < mla::kPage || topk_capacity % mla::kPage != 0)
+      return fail(MLA_ERR_UNSUPPORTED, "topk_capacity %d must be a positive multiple of 64", topk_capacity);
+    if (causal) return fail(MLA_ERR_UNSUPPORTED, "packed FP8 decode has no causal mask");
+  } else {
+    if (!block_table) return fail(MLA_ERR_INVALID_ARGUMENT, "block_table is NULL");
+    if (max_pages < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "max_pages %d < 1", max_pages);
+    if (num_pages < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "num_pages %lld < 1", (long long)num_pages);
+    if ((int64_t)batch * max_pages > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "batch * max_pages above 2^31");
+    if ((int64_t)max_pages * mla::kPage > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "max_pages too large");
+  }
+  if (num_parts < 1 || num_parts > MLA_MAX_PARTS)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "num_parts %d out of [1, %d]", num_parts, MLA_MAX_PARTS);
+  if (!(softmax_scale == softmax_scale)) return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale is NaN");
+  const size_t need = mla_decode_workspace_size(batch, s_q, h_q, num_parts);
+  if (!workspace || workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "decode workspace %zu B < %zu B", workspace_bytes, need);
+  st = check_device();
+  if (st) return st;
+
+  mla::DecodeArgs a;
+  a.q = (const uint16_t*)q;
+  a.kv = (const uint8_t*)kv;
+  a.num_pages = num_pages;
+  a.block_table = block_table;
+  a.max_pages = max_pages;
+  a.seqlens = seqlens;
+  a.cap = topk_capacity;
+  a.batch = batch;
+  a.s_q = s_q;
+  a.h_q = h_q;
+  a.M = s_q * h_q;
+  a.scale_log2 = softmax_scale * 1.44269504088896340736f;
+  a.causal = causal ? 1 : 0;
+  a.sched_meta = sched_meta;
+  a.num_splits = num_splits;
+  a.num_parts = num_parts;
+  a.out = (uint16_t*)out;
+  a.lse = lse;
+  a.slots = slots_for(batch, num_parts);
+  a.part_o = (float*)workspace;
+  a.part_lse = a.part_o + (size_t)a.slots * a.M * mla::kDV;
+  hipError_t e = mla::launch_decode(a, fp8, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
+}
+
+int mla_combine(const int32_t* num_splits, const void* workspace, size_t workspace_bytes, int batch, int s_q,
+                int h_q, int num_parts, void* out, float* lse, void* stream) {
+  if (!num_splits || !workspace || !out || !lse) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  int st = check_shape(batch, s_q, h_q, 1, MLA_KV_BF16_PAGED);
+  if (st) return st;
+  if (num_parts < 1 || num_parts > MLA_MAX_PARTS)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "num_parts %d out of [1, %d]", num_parts, MLA_MAX_PARTS);
+  const size_t need = mla_decode_workspace_size(batch, s_q, h_q, num_parts);
+  if (workspace_bytes < need) return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "decode workspace %zu B < %zu B", workspace_bytes, need);
+  st = check_device();
+  if (st) return st;
+  const int M = s_q * h_q;
+  const float* part_o = (const float*)workspace;
+  const float* part_lse = part_o + (size_t)slots_for(batch, num_parts) * M * mla::kDV;
+  hipError_t e = mla::launch_combine(num_splits, part_o, part_lse, batch, M, slots_for(batch, num_parts),
+                                     (uint16_t*)out, lse, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return ok();
+}
+
+int mla_pack_selected_kv(const void* kcache_fp8, int64_t num_pages, const int32_t* indices,
+                         const int32_t* topk_length, int batch, int s_q, int topk_capacity, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!kcache_fp8 || !indices || !topk_length || !workspace) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (batch < 1 || batch > MLA_MAX_BATCH) return fail(MLA_ERR_INVALID_ARGUMENT, "batch %d out of [1, %d]", batch, MLA_MAX_BATCH);
+  if (s_q < 1 || s_q > MLA_MAX_ROWS) return fail(MLA_ERR_INVALID_ARGUMENT, "s_q %d out of range", s_q);
+  if (num_pages < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "num_pages %lld < 1", (long long)num_pages);
+  if (topk_capacity < mla::kPage || topk_capacity % mla::kPage != 0)
+    return fail(MLA_ERR_UNSUPPORTED, "topk_capacity %d must be a positive multiple of 64", topk_capacity);
+  if ((int64_t)batch * s_q > 65535 || topk_capacity / mla::kPage > 65535)
+    return fail(MLA_ERR_UNSUPPORTED, "grid too large");
+  const size_t need = mla_packed_kv_workspace_size(batch, s_q, topk_capacity);
+  if (workspace_bytes < need) return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "packed workspace %zu B < %zu B", workspace_bytes, need);
+  int st = check_device();
+  if (st) return st;
+  hipError_t e = mla::launch_pack((const uint8_t*)kcache_fp8, num_pages, indices, topk_length, batch, s_q,
+                                  topk_capacity, (uint8_t*)workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "pack launch");
+  return ok();
+}
+
+int mla_read_device_errors(int* flags_out, void* stream) {
+  if (!flags_out) return fail(MLA_ERR_INVALID_ARGUMENT, "flags_out is NULL");
+  int st = check_device();
+  if (st) return st;
+  hipError_t e = mla::read_and_clear_error_flags(flags_out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "reading device flags");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Internal interface between the C ABI (mla_api.cpp) and the HIP kernels
+// (mla_kernels.hip).  Not installed; callers use include/mla_paged_kv.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kDQK = 576;
+constexpr int kDV = 512;
+constexpr int kPage = 64;
+constexpr int kRecBytes = 656;
+constexpr int kMaxRowsPerWG = 64;   // query rows (token, head) one decode workgroup covers
+constexpr int kDecodeThreads = 256; // 4 waves of 64
+constexpr int kSchedMaxBatch = 8192;
+
+// Device-side violation flags (see mla_read_device_errors).
+constexpr int kErrPage = 1;
+constexpr int kErrIndex = 2;
+constexpr int kErrSeqlen = 4;
+constexpr int kErrMeta = 8;
+
+struct DecodeArgs {
+  const uint16_t* q;          // bf16 bits [batch][s_q][h_q][576]
+  const uint8_t* kv;          // bf16 pages, or packed FP8 records
+  int64_t num_pages;
+  const int32_t* block_table; // [batch][max_pages]
+  int max_pages;
+  const int32_t* seqlens;     // [batch] (packed: topk_length)
+  int cap;                    // packed: top-k capacity (multiple of 64)
+  int batch, s_q, h_q, M;     // M = s_q * h_q rows per request
+  float scale_log2;           // softmax_scale * log2(e)
+  int causal;
+  const int32_t* sched_meta;  // [num_parts][8]
+  const int32_t* num_splits;  // [batch + 1]
+  int num_parts;
+  uint16_t* out;              // bf16 bits [batch][M][512]
+  float* lse;                 // [batch][M]
+  float* part_o;              // [slots][M][512]
+  float* part_lse;            // [slots][M]
+  int slots;
+};
+
+// Rows per workgroup for M rows per request: 16 * RB with RB in {1,2,4,8}.
+int decode_row_blocks_per_wg(int M);
+
+hipError_t launch_sched(const int32_t* lengths, int batch, int num_parts, int32_t* meta, int32_t* num_splits,
+                        hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, bool fp8, hipStream_t stream);
+hipError_t launch_combine(const int32_t* num_splits, const float* part_o, const float* part_lse, int batch, int M,
+                          int slots, uint16_t* out, float* lse, hipStream_t stream);
+hipError_t launch_pack(const uint8_t* kcache, int64_t num_pages, const int32_t* indices, const int32_t* topk_length,
+                       int batch, int s_q, int cap, uint8_t* ws, hipStream_t stream);
+hipError_t decode_occupancy(bool fp8, int M, int* wgs_per_cu);
+hipError_t read_and_clear_error_flags(int* flags, hipStream_t stream);
+
+}  // namespace mla

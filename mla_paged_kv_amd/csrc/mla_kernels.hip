@@ -1,0 +1,789 @@
+// HIP kernels for MLA decode over a paged KV cache on MI355X (gfx950, CDNA4).
+//
+// Method (FlashMLA PR 183 "Add SM80 (Ampere/A100) dense MLA decode kernel",
+// Summary/Design; FlashMLA PR 200 "[SM90] Add packed selected-KV sparse
+// decode", "SM90 packing kernel" / "Packed attention specialization"):
+// softmax(scale * Q K^T) V for s_q*h_q query rows that share one 576-dim latent
+// KV head, V = K[:, 0:512], keys in 64-token pages reached through a block
+// table, the sequence split over workgroups with an online softmax, and the
+// splits merged by a log-sum-exp combine.
+//
+// gfx950 design (not the pages' SM80/SM90 tiling):
+//   * One workgroup = 4 waves (one per SIMD) = up to 128 query rows of one
+//     partition.  Every 32-key tile is fetched from HBM once per workgroup and
+//     serves all rows, which is what makes QK^T and PV dense contractions.
+//   * K/V tiles (32 keys x 1152 B) stream HBM -> LDS with global_load_lds
+//     (16 B per lane, no VGPR staging) through a 4-stage ring; 16-B chunks of a
+//     key row are XOR-swizzled by (row & 7), which keeps the 16-rows-per-read
+//     MFMA operand fetches free of bank conflicts despite the 1152-B row pitch.
+//   * QK^T as S^T = K Q^T with v_mfma_f32_16x16x32_bf16: K is the A operand
+//     (ds_read_b128 from LDS), Q the B operand held in registers for the whole
+//     split (wave w owns rows [16w, 16w+16) and [16(w+4), ...)).
+//   * PV as O^T = V^T P^T: V^T comes from the same LDS tile through
+//     ds_read_b64_tr_b16 transposed reads, P^T (bf16) from a small LDS buffer;
+//     wave w owns output columns [128w, 128w+128) for all rows, so P is
+//     computed once per row and shared, and each V element is read once.
+//   * Online softmax in the exp2 domain with lazy rescaling: the running max
+//     moves (and O is rescaled) only when a tile's max exceeds it by more than
+//     kRescaleThreshold (log2 units); final out = O / l is exact either way.
+//   * The FP8 packed variant loads 656-byte records into a raw LDS ring and
+//     dequantises each tile (E4M3 x fp32 scale -> bf16; RoPE copied) into the
+//     same swizzled bf16 tile the dense path uses.
+#include "mla_internal.h"
+
+#include <math.h>
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+#define LDS_AS __attribute__((address_space(3)))
+
+__device__ int g_error_flags;
+
+// Read-only kernel inputs that every lane of a wave indexes the same way (page
+// table, lengths, scheduler records) are read through the constant address
+// space so that they become scalar loads: a vector load here would need a
+// vmcnt wait, and vmcnt retires in order, i.e. it would also wait for every
+// tile still in flight in the global->LDS ring.
+template <class T>
+using const_ptr = const __attribute__((address_space(4))) T*;
+template <class T>
+__device__ __forceinline__ T ld_const(const T* p, int64_t i) {
+  return ((const_ptr<T>)(p))[i];
+}
+
+// ------------------------------------------------------------------ decode geometry
+constexpr int kTK = 32;                             // keys per tile
+constexpr int kStages = 4;                          // HBM -> LDS ring depth
+constexpr int kRowBytes = kDQK * 2;                 // 1152
+constexpr int kTileBytes = kTK * kRowBytes;         // 36864
+constexpr int kChunksPerRow = kRowBytes / 16;       // 72
+constexpr int kLoadsPerWave = kTileBytes / 1024 / 4;  // 9 wave-wide 16-B loads per tile per wave
+constexpr int kPStride = kTK * 2 + 16;              // P row pitch (bytes), padded against bank conflicts
+constexpr int kRawTileBytes = 24 * 1024;            // FP8 raw tile slot (32 x 656 = 20992 B used)
+constexpr int kRawLoadsPerWave = 6;                 // 24 wave-wide loads per raw tile
+constexpr int kRawChunks = kTK * kRecBytes / 16;    // 1312
+constexpr float kRescaleThreshold = 8.0f;           // log2 units: p <= 2^8 between rescales
+
+// LDS layout
+constexpr int kPBufBytes = kMaxRowsPerWG * kPStride;            // one P buffer (5 KB)
+constexpr int kOffKDense = 0;
+constexpr int kOffRaw = 0;                                      // FP8: raw ring
+constexpr int kOffKFp8 = kStages * kRawTileBytes;               // FP8: widened bf16 tile
+constexpr int kOffPDense = kStages * kTileBytes;                // 147456
+constexpr int kOffPFp8 = kOffKFp8 + kTileBytes;                 // 135168
+__host__ __device__ constexpr int off_p(bool fp8) { return fp8 ? kOffPFp8 : kOffPDense; }
+__host__ __device__ constexpr int off_alpha(bool fp8) { return off_p(fp8) + (fp8 ? 4 : 1) * kPBufBytes; }
+__host__ __device__ constexpr int off_flag(bool fp8) { return off_alpha(fp8) + kMaxRowsPerWG * 4; }
+__host__ __device__ constexpr int off_l(bool fp8) { return off_flag(fp8) + 64; }
+__host__ __device__ constexpr int lds_bytes(bool fp8) { return off_l(fp8) + kMaxRowsPerWG * 4; }
+static_assert(lds_bytes(false) <= 160 * 1024, "dense LDS budget");
+static_assert(lds_bytes(true) <= 160 * 1024, "fp8 LDS budget");
+
+// ------------------------------------------------------------------ small device helpers
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Barrier that also makes this wave's LDS writes visible.  No vmcnt wait: the
+// global->LDS ring is waited for explicitly with wait_vmcnt.
+__device__ __forceinline__ void sync_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void load_lds16(const void* gsrc, LDS_AS void* ldst) {
+  __builtin_amdgcn_global_load_lds(gsrc, ldst, 16, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const LDS_AS uint8_t* p) {
+  return *reinterpret_cast<const LDS_AS bf16x8*>(p);
+}
+
+// Transposed 4 x 16 read (ds_read_b64_tr_b16): in each 16-lane group, lanes
+// 4r..4r+3 address the 16 consecutive bf16 of row r (4 each); lane i receives
+// column i of rows 0..3.  Issued through inline asm: the compiler does not know
+// this intrinsic cannot alias the in-flight global->LDS loads and would
+// otherwise put a vmcnt(0) in front of it.  The caller must call
+// lds_wait_tr16() on the result before using it.
+__device__ __forceinline__ u32x2 lds_read_tr16(const LDS_AS uint8_t* p) {
+  u32x2 r;
+  const uint32_t addr = (uint32_t)(uintptr_t)p;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+  return r;
+}
+__device__ __forceinline__ void lds_wait_tr16(u32x2& a, u32x2& b) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b)::"memory");
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+__device__ __forceinline__ float wave_xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
+__device__ __forceinline__ float wave_xor_sum(float v, int mask) { return v + __shfl_xor(v, mask, 64); }
+
+// byte offset of (key row kr, 16-B chunk c) inside a swizzled bf16 tile
+__device__ __forceinline__ uint32_t tile_off(int kr, int c) {
+  return (uint32_t)(kr * kRowBytes + ((c ^ (kr & 7)) << 4));
+}
+
+// ------------------------------------------------------------------ scheduler
+// One workgroup.  Implements the partition definition in mla_paged_kv.h: request r
+// has ceil(len/64) blocks, T in all; with P' = min(P, T), part p < P' owns global
+// blocks [floor(pT/P'), floor((p+1)T/P')) and parts p >= P' own none, so the
+// parts owning one request's blocks are consecutive.
+constexpr int kSchedThreads = 1024;
+
+__device__ __forceinline__ int64_t part_of_block(int64_t g, int64_t T, int64_t P) { return ((g + 1) * P - 1) / T; }
+
+__global__ __launch_bounds__(kSchedThreads) void sched_kernel(const int32_t* __restrict__ lengths, int batch,
+                                                              int num_parts, int32_t* __restrict__ meta,
+                                                              int32_t* __restrict__ num_splits) {
+  __shared__ int32_t cum[kSchedMaxBatch + 1];
+  __shared__ int32_t scan[kSchedThreads];
+  const int t = threadIdx.x;
+  const int C = (batch + kSchedThreads - 1) / kSchedThreads;  // <= 8
+
+  // 1. blocks per request, exclusive prefix -> cum
+  int local = 0;
+  for (int k = 0; k < C; ++k) {
+    int r = t * C + k;
+    if (r < batch) local += (max(lengths[r], 0) + kPage - 1) / kPage;
+  }
+  scan[t] = local;
+  __syncthreads();
+  for (int off = 1; off < kSchedThreads; off <<= 1) {
+    int v = t >= off ? scan[t - off] : 0;
+    __syncthreads();
+    scan[t] += v;
+    __syncthreads();
+  }
+  int run = scan[t] - local;
+  for (int k = 0; k < C; ++k) {
+    int r = t * C + k;
+    if (r < batch) {
+      cum[r] = run;
+      run += (max(lengths[r], 0) + kPage - 1) / kPage;
+    }
+  }
+  if (t == kSchedThreads - 1) cum[batch] = scan[t];
+  __syncthreads();
+  const int64_t T = cum[batch];
+  const int64_t P = T < num_parts ? T : num_parts;  // P' (0 when there is no block at all)
+
+  // 2. partition records
+  for (int p = t; p < num_parts; p += kSchedThreads) {
+    int32_t* m = meta + (int64_t)p * 8;
+    const int64_t G0 = p < P ? ((int64_t)p * T) / P : T;
+    const int64_t G1 = p < P ? ((int64_t)(p + 1) * T) / P : T;
+    if (G1 <= G0) {
+      m[0] = m[1] = m[2] = m[3] = m[4] = -1;
+    } else {
+      // first request whose block range ends after G0 (resp. after G1 - 1)
+      int lo = 0, hi = batch - 1;
+      while (lo < hi) {
+        int mid = (lo + hi) >> 1;
+        if (cum[mid + 1] > G0) hi = mid; else lo = mid + 1;
+      }
+      const int br = lo;
+      lo = br;
+      hi = batch - 1;
+      while (lo < hi) {
+        int mid = (lo + hi) >> 1;
+        if (cum[mid + 1] >= G1) hi = mid; else lo = mid + 1;
+      }
+      const int er = lo;
+      m[0] = br;
+      m[1] = (int32_t)(G0 - cum[br]);
+      m[2] = er;
+      m[3] = (int32_t)(G1 - cum[er]);
+      m[4] = (int32_t)(p - part_of_block(cum[br], T, P));
+    }
+    m[5] = m[6] = m[7] = 0;
+  }
+
+  // 3. split counts, exclusive prefix -> num_splits
+  int splits_local = 0;
+  for (int k = 0; k < C; ++k) {
+    int r = t * C + k;
+    if (r < batch && cum[r + 1] > cum[r])
+      splits_local += (int)(part_of_block(cum[r + 1] - 1, T, P) - part_of_block(cum[r], T, P) + 1);
+  }
+  __syncthreads();
+  scan[t] = splits_local;
+  __syncthreads();
+  for (int off = 1; off < kSchedThreads; off <<= 1) {
+    int v = t >= off ? scan[t - off] : 0;
+    __syncthreads();
+    scan[t] += v;
+    __syncthreads();
+  }
+  run = scan[t] - splits_local;
+  for (int k = 0; k < C; ++k) {
+    int r = t * C + k;
+    if (r < batch) {
+      num_splits[r] = run;
+      if (cum[r + 1] > cum[r]) run += (int)(part_of_block(cum[r + 1] - 1, T, P) - part_of_block(cum[r], T, P) + 1);
+    }
+  }
+  if (t == kSchedThreads - 1) num_splits[batch] = scan[t];
+}
+
+// ------------------------------------------------------------------ decode
+template <bool FP8>
+struct TileLoader;
+
+// bf16 pages: tile = 32 consecutive keys of one 64-token page (36,864 contiguous bytes).
+template <>
+struct TileLoader<false> {
+  uint32_t off[kLoadsPerWave];  // per-lane source offset inside the tile for each of this wave's loads
+  __device__ void init(int w, int l) {
+#pragma unroll
+    for (int k = 0; k < kLoadsPerWave; ++k) {
+      int qi = w + 4 * k;           // wave-wide load index within the tile (0..35)
+      int p = qi * 64 + l;          // destination 16-B chunk position in the tile
+      int kr = p / kChunksPerRow;
+      int pos = p - kr * kChunksPerRow;
+      int c = pos ^ (kr & 7);       // logical chunk stored at that position
+      off[k] = (uint32_t)(kr * kRowBytes + c * 16);
+    }
+  }
+  // Issues this wave's loads of tile `tile` of request r into stage `st`.
+  __device__ void issue(const DecodeArgs& a, int r, int key0, LDS_AS uint8_t* smem, int st, int w) {
+    int64_t page = ld_const(a.block_table, (int64_t)r * a.max_pages + (key0 >> 6));
+    if (page < 0 || page >= a.num_pages) {
+      if ((threadIdx.x & 63) == 0) atomicOr(&g_error_flags, kErrPage);
+      page = 0;  // stay in bounds; the output of this request is undefined
+    }
+    const uint8_t* src = a.kv + page * (int64_t)(kPage * kRowBytes) + (key0 & 63) * kRowBytes;
+    LDS_AS uint8_t* dst = smem + kOffKDense + st * kTileBytes;
+#pragma unroll
+    for (int k = 0; k < kLoadsPerWave; ++k) load_lds16(src + off[k], dst + (w + 4 * k) * 1024);
+  }
+};
+
+// FP8 packed workspace: tile = 32 consecutive 656-byte records of one query row.
+template <>
+struct TileLoader<true> {
+  uint32_t off[kRawLoadsPerWave];
+  __device__ void init(int w, int l) {
+#pragma unroll
+    for (int k = 0; k < kRawLoadsPerWave; ++k) {
+      int p = (w + 4 * k) * 64 + l;  // 16-B chunk position in the raw slot (0..1535)
+      // positions past the 1312 real chunks re-read chunk 0 (keeps every wave's
+      // load count uniform for the vmcnt bookkeeping; lands in unused LDS)
+      off[k] = (uint32_t)((p < kRawChunks ? p : 0) * 16);
+    }
+  }
+  __device__ void issue(const DecodeArgs& a, int r, int key0, LDS_AS uint8_t* smem, int st, int w) {
+    const uint8_t* src = a.kv + ((int64_t)r * a.cap + key0) * kRecBytes;
+    LDS_AS uint8_t* dst = smem + kOffRaw + st * kRawTileBytes;
+#pragma unroll
+    for (int k = 0; k < kRawLoadsPerWave; ++k) load_lds16(src + off[k], dst + (w + 4 * k) * 1024);
+  }
+};
+
+// Widen a raw FP8 tile into the swizzled bf16 tile: NoPE bytes E4M3 -> bf16 (exact:
+// every E4M3 value is a bf16 value; the per-block fp32 scales are applied later,
+// in fp32, to the scores and to P), RoPE copied.  Rows >= nvalid become zero.
+__device__ __forceinline__ void widen_fp8_tile(const LDS_AS uint8_t* raw, LDS_AS uint8_t* kt, int nvalid) {
+  for (int idx = threadIdx.x; idx < kTK * kChunksPerRow; idx += kDecodeThreads) {
+    const int kr = idx / kChunksPerRow;
+    const int c = idx - kr * kChunksPerRow;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (kr < nvalid) {
+      const LDS_AS uint8_t* rec = raw + kr * kRecBytes;
+      if (c < 64) {
+        const u32x2 codes = *reinterpret_cast<const LDS_AS u32x2*>(rec + c * 8);
+        const f32x2 f0 = __builtin_amdgcn_cvt_pk_f32_fp8(codes.x, false);
+        const f32x2 f1 = __builtin_amdgcn_cvt_pk_f32_fp8(codes.x, true);
+        const f32x2 f2 = __builtin_amdgcn_cvt_pk_f32_fp8(codes.y, false);
+        const f32x2 f3 = __builtin_amdgcn_cvt_pk_f32_fp8(codes.y, true);
+        v = u32x4{(uint32_t)f32_to_bf16_rne(f0.x) | ((uint32_t)f32_to_bf16_rne(f0.y) << 16),
+                  (uint32_t)f32_to_bf16_rne(f1.x) | ((uint32_t)f32_to_bf16_rne(f1.y) << 16),
+                  (uint32_t)f32_to_bf16_rne(f2.x) | ((uint32_t)f32_to_bf16_rne(f2.y) << 16),
+                  (uint32_t)f32_to_bf16_rne(f3.x) | ((uint32_t)f32_to_bf16_rne(f3.y) << 16)};
+      } else {
+        v = *reinterpret_cast<const LDS_AS u32x4*>(rec + 528 + (c - 64) * 16);
+      }
+    }
+    *reinterpret_cast<LDS_AS u32x4*>(kt + tile_off(kr, c)) = v;
+  }
+}
+
+// Zero V rows [nvalid, 32) of a bf16 tile (keys past the end of the sequence may
+// hold anything, and 0 * NaN would poison PV).
+__device__ __forceinline__ void zero_tail_rows(LDS_AS uint8_t* kt, int nvalid) {
+  const int n = (kTK - nvalid) * 64;  // 16-B chunks of the 512 V dims
+  for (int idx = threadIdx.x; idx < n; idx += kDecodeThreads) {
+    int kr = nvalid + (idx >> 6);
+    int c = idx & 63;
+    *reinterpret_cast<LDS_AS u32x4*>(kt + tile_off(kr, c)) = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
+}
+
+// One workgroup: the 16*RB query rows of row block blockIdx.y, over the KV range
+// of partition blockIdx.x.  Wave w computes scores for rows [16w, 16w+16) (if
+// w < RB) and accumulates output columns [128w, 128w+128) for all rows.
+template <int RB, bool FP8>
+__global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a) {
+  constexpr int MB = 16 * RB;  // rows per workgroup
+  static_assert(MB <= kMaxRowsPerWG, "row block");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[lds_bytes(FP8)];
+  LDS_AS uint8_t* smem = (LDS_AS uint8_t*)(smem_raw);  // C-style: generic -> LDS address space
+  LDS_AS uint8_t* pbuf = smem + off_p(FP8);
+  LDS_AS float* alpha_s = reinterpret_cast<LDS_AS float*>(smem + off_alpha(FP8));
+  LDS_AS int* flag_s = reinterpret_cast<LDS_AS int*>(smem + off_flag(FP8));
+  LDS_AS float* l_s = reinterpret_cast<LDS_AS float*>(smem + off_l(FP8));
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, g = l >> 4, li = l & 15;
+  const bool qk_wave = w < RB;
+  const int part = blockIdx.x, rbk = blockIdx.y;
+  const int begin_req = ld_const(a.sched_meta, part * 8 + 0);
+  if (begin_req < 0) return;
+  const int begin_blk = ld_const(a.sched_meta, part * 8 + 1);
+  const int end_req = ld_const(a.sched_meta, part * 8 + 2);
+  const int end_blk = ld_const(a.sched_meta, part * 8 + 3);
+  const int begin_split = ld_const(a.sched_meta, part * 8 + 4);
+  if (begin_req >= a.batch || end_req >= a.batch || end_req < begin_req) {  // not a scheduler record
+    if (threadIdx.x == 0) atomicOr(&g_error_flags, kErrMeta);
+    return;
+  }
+
+  TileLoader<FP8> loader;
+  loader.init(w, l);
+
+  // QK^T: per-lane K-operand byte offsets for even/odd 32-dim k-steps (see tile_off):
+  // row li (+16 for the second key block), chunk 4s+g stored at (4s+g)^(li&7).
+  const int kx = li & 7;
+  const uint32_t kq_base0 = (uint32_t)(li * kRowBytes + 16 * (4 * (0 ^ (kx >> 2)) + (g ^ (kx & 3))));
+  const uint32_t kq_base1 = (uint32_t)(li * kRowBytes + 16 * (4 * (1 ^ (kx >> 2)) + (g ^ (kx & 3))));
+  // PV: transposed V reads; lane (4r + j) of group g addresses key 8g + r (+4), dims 4j.. of a 16-dim block
+  const int tr_r = li >> 2, tr_j = li & 3;
+  // this wave's P buffer: FP8 keeps one per 128-column scale block (P times that block's scale)
+  LDS_AS uint8_t* pmine = pbuf + (FP8 ? w * kPBufBytes : 0);
+  const int row_local = 16 * w + li;  // this lane's score row within the workgroup (if qk_wave)
+
+  for (int r = begin_req; r <= end_req; ++r) {
+    int seqlen = ld_const(a.seqlens, r);
+    if (seqlen < 0 || (!FP8 && seqlen > a.max_pages * kPage) || (FP8 && seqlen > a.cap)) {
+      if (tid == 0) atomicOr(&g_error_flags, kErrSeqlen);
+      seqlen = seqlen < 0 ? 0 : (FP8 ? a.cap : a.max_pages * kPage);
+    }
+    const int nblk = (seqlen + kPage - 1) / kPage;
+    const int blk0 = (r == begin_req) ? begin_blk : 0;
+    const int blk1 = (r == end_req) ? end_blk : nblk;
+    const int t0 = blk0 * kPage;
+    const int t1 = min(blk1 * kPage, seqlen);
+    const int ntile = t1 > t0 ? (t1 - t0 + kTK - 1) / kTK : 0;
+    const int split = (r == begin_req) ? begin_split : 0;
+    const int ns0 = ld_const(a.num_splits, r);
+    const int nsplit = ld_const(a.num_splits, r + 1) - ns0;
+    const int slot = ns0 + split;
+    if (nsplit > 1 && (slot < 0 || slot >= a.slots)) {  // inconsistent metadata: skip, never write out of range
+      if (threadIdx.x == 0) atomicOr(&g_error_flags, kErrMeta);
+      continue;
+    }
+
+    // ---- Q rows (B operand of S^T = K Q^T), visible-key limit, softmax state
+    const int rho = rbk * MB + row_local;  // row within the request
+    const bool live = qk_wave && rho < a.M;
+    bf16x8 qreg[18];
+    {
+      const uint16_t* qrow = a.q + ((int64_t)r * a.M + (live ? rho : 0)) * kDQK + 8 * g;
+#pragma unroll
+      for (int s = 0; s < 18; ++s) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 32 * s);
+        qreg[s] = live ? v : bf16x8{};
+      }
+    }
+    int lim = 0;
+    if (live) {
+      int nvis = seqlen;
+      if (a.causal) nvis = min(max(seqlen - a.s_q + rho / a.h_q + 1, 0), seqlen);
+      lim = min(t1, nvis);
+    }
+    float mrow = -INFINITY, lpart = 0.f;
+    f32x4 o[8][RB];
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // ---- pipeline prologue: tiles 0 .. kStages-2
+#pragma unroll
+    for (int tt = 0; tt < kStages - 1; ++tt)
+      if (tt < ntile) loader.issue(a, r, t0 + tt * kTK, smem, tt, w);
+
+    for (int tile = 0; tile < ntile; ++tile) {
+      // own loads of this tile done (later tiles may stay in flight) ...
+      constexpr int LPW = FP8 ? kRawLoadsPerWave : kLoadsPerWave;
+      if (tile + 2 < ntile) wait_vmcnt<2 * LPW>();
+      else if (tile + 1 < ntile) wait_vmcnt<LPW>();
+      else wait_vmcnt<0>();
+      // ... and everyone's, and every wave is past PV of the previous tile
+      sync_lds();
+      if (tile + kStages - 1 < ntile)
+        loader.issue(a, r, t0 + (tile + kStages - 1) * kTK, smem, (tile + kStages - 1) % kStages, w);
+
+      const int key0 = t0 + tile * kTK;
+      const int nvalid = min(kTK, t1 - key0);
+      LDS_AS uint8_t* kt;
+      const LDS_AS uint8_t* raw = nullptr;
+      if constexpr (FP8) {
+        raw = smem + kOffRaw + (tile % kStages) * kRawTileBytes;
+        kt = smem + kOffKFp8;
+        widen_fp8_tile(raw, kt, nvalid);
+        sync_lds();
+      } else {
+        kt = smem + kOffKDense + (tile % kStages) * kTileBytes;
+        if (nvalid < kTK) zero_tail_rows(kt, nvalid);
+      }
+
+      // ---- phase A: S^T = K Q^T for this wave's 16 rows, online softmax, P -> LDS
+      if (qk_wave) {
+        // FP8: the four 128-dim NoPE blocks and the RoPE part accumulate apart
+        // (groups 0..3, 4) so that each key's block scales multiply exact sums.
+        constexpr int NG = FP8 ? 5 : 1;
+        f32x4 acc[2][NG];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int gi = 0; gi < NG; ++gi) acc[kb][gi] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // software pipeline over the 18 k-steps: operands of step s+1 are in
+        // flight while step s multiplies; the scheduling barriers stop the
+        // compiler from hoisting all 36 LDS reads (and their registers) up front
+        bf16x8 cur0 = lds_read_b128(kt + kq_base0);
+        bf16x8 cur1 = lds_read_b128(kt + kq_base0 + 16 * kRowBytes);
+#pragma unroll
+        for (int s = 0; s < 18; ++s) {
+          bf16x8 nxt0 = cur0, nxt1 = cur1;
+          if (s + 1 < 18) {
+            const uint32_t nb = (((s + 1) & 1) ? kq_base1 : kq_base0) + ((s + 1) >> 1) * 128;
+            nxt0 = lds_read_b128(kt + nb);
+            nxt1 = lds_read_b128(kt + nb + 16 * kRowBytes);
+          }
+          const int gi = FP8 ? (s < 16 ? (s >> 2) : 4) : 0;
+          acc[0][gi] = mfma16(cur0, qreg[s], acc[0][gi]);
+          acc[1][gi] = mfma16(cur1, qreg[s], acc[1][gi]);
+          cur0 = nxt0;
+          cur1 = nxt1;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // lane holds scores of row row_local for keys 16kb + 4g + i
+        float sv[8];
+        f32x4 ksc[8];  // FP8: the 4 block scales of each of those keys
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kr = 16 * kb + 4 * g + i;
+            float x;
+            if constexpr (FP8) {
+              // keys past the valid prefix get scale 0 (their bytes are not guaranteed finite)
+              ksc[kb * 4 + i] = kr < nvalid ? *reinterpret_cast<const LDS_AS f32x4*>(raw + kr * kRecBytes + 512)
+                                            : f32x4{0.f, 0.f, 0.f, 0.f};
+              const f32x4 sc = ksc[kb * 4 + i];
+              x = acc[kb][NG - 1][i] + sc[0] * acc[kb][0][i] + sc[1] * acc[kb][1 % NG][i] +
+                  sc[2] * acc[kb][2 % NG][i] + sc[3] * acc[kb][3 % NG][i];
+            } else {
+              x = acc[kb][0][i];
+            }
+            x *= a.scale_log2;
+            sv[kb * 4 + i] = key0 + kr < lim ? x : -INFINITY;
+            mx = fmaxf(mx, sv[kb * 4 + i]);
+          }
+        mx = wave_xor_max(mx, 16);
+        mx = wave_xor_max(mx, 32);
+        const float mold = mrow;
+        const bool upd = mx > mold + kRescaleThreshold;
+        const float mnew = upd ? mx : mold;
+        const float alpha = upd ? fast_exp2(mold - mnew) : 1.f;
+        mrow = mnew;
+        const float mref = (mnew == -INFINITY) ? 0.f : mnew;
+        float pv[8];
+        float psum = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          pv[k] = fast_exp2(sv[k] - mref);
+          psum += pv[k];
+        }
+        lpart = lpart * alpha + psum;
+        // P[row][key] (bf16): keys 4g..4g+3 at byte 8g, keys 16+4g.. at byte 32+8g
+        if constexpr (FP8) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            LDS_AS uint8_t* prow = pbuf + b * kPBufBytes + row_local * kPStride + 8 * g;
+            *reinterpret_cast<LDS_AS u32x2*>(prow) =
+                u32x2{pack_bf16x2(pv[0] * ksc[0][b], pv[1] * ksc[1][b]), pack_bf16x2(pv[2] * ksc[2][b], pv[3] * ksc[3][b])};
+            *reinterpret_cast<LDS_AS u32x2*>(prow + 32) =
+                u32x2{pack_bf16x2(pv[4] * ksc[4][b], pv[5] * ksc[5][b]), pack_bf16x2(pv[6] * ksc[6][b], pv[7] * ksc[7][b])};
+          }
+        } else {
+          LDS_AS uint8_t* prow = pbuf + row_local * kPStride + 8 * g;
+          *reinterpret_cast<LDS_AS u32x2*>(prow) = u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
+          *reinterpret_cast<LDS_AS u32x2*>(prow + 32) = u32x2{pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
+        }
+        if (g == 0) alpha_s[row_local] = alpha;
+        const bool any = __any(upd);
+        if (l == 0) flag_s[w] = any ? 1 : 0;
+      }
+      sync_lds();
+
+      // ---- phase B: O^T[cols of wave w] += V^T P^T for all rows
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        if (flag_s[rb]) {
+          const float al = alpha_s[16 * rb + li];
+#pragma unroll
+          for (int db = 0; db < 8; ++db) o[db][rb] *= al;
+        }
+      }
+      bf16x8 bp[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) bp[rb] = lds_read_b128(pmine + (16 * rb + li) * kPStride + 16 * g);
+      const int kr0 = 8 * g + tr_r;
+      const uint32_t within = (tr_j & 1) * 8;
+      // V^T operand of dim block db (16 columns): keys 8g..8g+7 of column 128w+16db+li
+      auto vt_issue = [&](int db, u32x2& v0, u32x2& v1) {
+        const int c = 16 * w + 2 * db + (tr_j >> 1);  // chunk holding dims 128w + 16db + 4j ..
+        v0 = lds_read_tr16(kt + tile_off(kr0, c) + within);
+        v1 = lds_read_tr16(kt + tile_off(kr0 + 4, c) + within);
+      };
+      u32x2 c0, c1;
+      vt_issue(0, c0, c1);
+      lds_wait_tr16(c0, c1);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        u32x2 n0 = c0, n1 = c1;
+        if (db + 1 < 8) vt_issue(db + 1, n0, n1);
+        const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{c0.x, c0.y, c1.x, c1.y});
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) o[db][rb] = mfma16(av, bp[rb], o[db][rb]);
+        if (db + 1 < 8) lds_wait_tr16(n0, n1);
+        c0 = n0;
+        c1 = n1;
+      }
+    }
+
+    // ---- epilogue: row sums to LDS, then normalise and store
+    if (qk_wave) {
+      float lt = wave_xor_sum(lpart, 16);
+      lt = wave_xor_sum(lt, 32);
+      if (g == 0) {
+        l_s[row_local] = lt;
+        if (rho < a.M) {
+          const float lse = lt > 0.f ? (mrow + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
+          if (nsplit == 1) a.lse[(int64_t)r * a.M + rho] = lse;
+          else a.part_lse[(int64_t)slot * a.M + rho] = lse;
+        }
+      }
+    }
+    sync_lds();
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int rho_o = rbk * MB + 16 * rb + li;
+      if (rho_o >= a.M) continue;
+      const float lt = l_s[16 * rb + li];
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      if (nsplit == 1) {
+        uint16_t* orow = a.out + ((int64_t)r * a.M + rho_o) * kDV + 128 * w + 4 * g;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const f32x4 v = o[db][rb] * inv;
+          *reinterpret_cast<u32x2*>(orow + 16 * db) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        }
+      } else {
+        float* prow = a.part_o + ((int64_t)slot * a.M + rho_o) * kDV + 128 * w + 4 * g;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(prow + 16 * db) = o[db][rb] * inv;
+      }
+    }
+    // the next request of this partition reuses every LDS buffer: all waves are
+    // past the last PV and the l reads once they pass this barrier; its first
+    // loads must not overtake this request's stores in the vmcnt count
+    wait_vmcnt<0>();
+    sync_lds();
+  }
+}
+
+// 16-row blocks per workgroup.  Capped at 4 (64 rows): at 128 rows the Q and O
+// register tiles alone take ~400 of a wave's 512 registers and the compiler
+// spills; an h_q = 128 request is covered by two 64-row workgroups whose
+// shared KV tiles meet in L2.
+int decode_row_blocks_per_wg(int M) {
+  int rb = (M + 15) / 16;
+  if (rb <= 1) return 1;
+  if (rb <= 2) return 2;
+  return 4;
+}
+
+template <int RB, bool FP8>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+  const int MB = 16 * RB;
+  dim3 grid(a.num_parts, (a.M + MB - 1) / MB);
+  hipLaunchKernelGGL((decode_kernel<RB, FP8>), grid, dim3(kDecodeThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, bool fp8, hipStream_t stream) {
+  switch (decode_row_blocks_per_wg(a.M)) {
+    case 1: return fp8 ? launch_decode_t<1, true>(a, stream) : launch_decode_t<1, false>(a, stream);
+    case 2: return fp8 ? launch_decode_t<2, true>(a, stream) : launch_decode_t<2, false>(a, stream);
+    default: return fp8 ? launch_decode_t<4, true>(a, stream) : launch_decode_t<4, false>(a, stream);
+  }
+}
+
+hipError_t decode_occupancy(bool fp8, int M, int* wgs_per_cu) {
+  int n = 0;
+  hipError_t e;
+  switch (decode_row_blocks_per_wg(M)) {
+    case 1: e = fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<1, true>, kDecodeThreads, 0)
+                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<1, false>, kDecodeThreads, 0);
+      break;
+    case 2: e = fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<2, true>, kDecodeThreads, 0)
+                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<2, false>, kDecodeThreads, 0);
+      break;
+    default: e = fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<4, true>, kDecodeThreads, 0)
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<4, false>, kDecodeThreads, 0);
+      break;
+  }
+  *wgs_per_cu = n;
+  return e;
+}
+
+// ------------------------------------------------------------------ combine
+// One wave per (request, row); lane l owns output columns [8l, 8l+8).
+__global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ num_splits,
+                                                      const float* __restrict__ part_o,
+                                                      const float* __restrict__ part_lse, int M, int slots,
+                                                      uint16_t* __restrict__ out, float* __restrict__ lse) {
+  const int r = blockIdx.x;
+  const int rho = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  if (rho >= M) return;
+  const int s0 = num_splits[r];
+  const int S = num_splits[r + 1] - s0;
+  if (S == 1) return;
+  if (s0 < 0 || S < 0 || s0 + S > slots) {  // not scheduler output: never read out of range
+    if (threadIdx.x == 0) atomicOr(&g_error_flags, kErrMeta);
+    return;
+  }
+  uint16_t* orow = out + ((int64_t)r * M + rho) * kDV + 8 * l;
+  float mx = -INFINITY;
+  for (int i = 0; i < S; ++i) mx = fmaxf(mx, part_lse[(int64_t)(s0 + i) * M + rho]);
+  if (mx == -INFINITY) {  // no split saw a key (or no split at all)
+    *reinterpret_cast<u32x4*>(orow) = u32x4{0u, 0u, 0u, 0u};
+    if (l == 0) lse[(int64_t)r * M + rho] = -INFINITY;
+    return;
+  }
+  float tot = 0.f;
+  for (int i = 0; i < S; ++i) tot += expf(part_lse[(int64_t)(s0 + i) * M + rho] - mx);
+  const float L = mx + logf(tot);
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < S; ++i) {
+    const float wgt = expf(part_lse[(int64_t)(s0 + i) * M + rho] - L);
+    const float* src = part_o + ((int64_t)(s0 + i) * M + rho) * kDV + 8 * l;
+    acc0 += wgt * *reinterpret_cast<const f32x4*>(src);
+    acc1 += wgt * *reinterpret_cast<const f32x4*>(src + 4);
+  }
+  u32x4 pk;
+  pk.x = (uint32_t)f32_to_bf16_rne(acc0[0]) | ((uint32_t)f32_to_bf16_rne(acc0[1]) << 16);
+  pk.y = (uint32_t)f32_to_bf16_rne(acc0[2]) | ((uint32_t)f32_to_bf16_rne(acc0[3]) << 16);
+  pk.z = (uint32_t)f32_to_bf16_rne(acc1[0]) | ((uint32_t)f32_to_bf16_rne(acc1[1]) << 16);
+  pk.w = (uint32_t)f32_to_bf16_rne(acc1[2]) | ((uint32_t)f32_to_bf16_rne(acc1[3]) << 16);
+  *reinterpret_cast<u32x4*>(orow) = pk;
+  if (l == 0) lse[(int64_t)r * M + rho] = L;
+}
+
+// ------------------------------------------------------------------ pack
+// One workgroup per (query row, 64-record tile); 16-B chunks, 41 per record.
+__global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ kcache, int64_t num_pages,
+                                                   const int32_t* __restrict__ indices,
+                                                   const int32_t* __restrict__ topk_length, int s_q, int cap,
+                                                   uint8_t* __restrict__ ws) {
+  constexpr int kChunksPerRec = kRecBytes / 16;  // 41
+  const int row = blockIdx.x;                    // r * s_q + i
+  const int tile = blockIdx.y;
+  const int r = row / s_q;
+  int n = topk_length[r];
+  if (n < 0 || n > cap) {
+    if (threadIdx.x == 0) atomicOr(&g_error_flags, kErrSeqlen);
+    n = n < 0 ? 0 : cap;
+  }
+  const int32_t* idx = indices + (int64_t)row * cap + tile * kPage;
+  uint8_t* dst = ws + ((int64_t)row * cap + (int64_t)tile * kPage) * kRecBytes;
+  const int64_t limit = num_pages * kPage;
+  for (int c = threadIdx.x; c < kPage * kChunksPerRec; c += 256) {
+    const int k = c / kChunksPerRec;
+    const int piece = c - k * kChunksPerRec;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (tile * kPage + k < n) {
+      const int64_t id = idx[k];
+      if (id >= 0 && id < limit) {
+        v = *reinterpret_cast<const u32x4*>(kcache + id * kRecBytes + piece * 16);
+      } else if (piece == 0) {
+        atomicOr(&g_error_flags, kErrIndex);
+      }
+    }
+    *reinterpret_cast<u32x4*>(dst + (int64_t)c * 16) = v;
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+hipError_t launch_sched(const int32_t* lengths, int batch, int num_parts, int32_t* meta, int32_t* num_splits,
+                        hipStream_t stream) {
+  hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kSchedThreads), 0, stream, lengths, batch, num_parts, meta,
+                     num_splits);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const int32_t* num_splits, const float* part_o, const float* part_lse, int batch, int M,
+                          int slots, uint16_t* out, float* lse, hipStream_t stream) {
+  dim3 grid(batch, (M + 3) / 4);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, stream, num_splits, part_o, part_lse, M, slots, out, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(const uint8_t* kcache, int64_t num_pages, const int32_t* indices, const int32_t* topk_length,
+                       int batch, int s_q, int cap, uint8_t* ws, hipStream_t stream) {
+  dim3 grid(batch * s_q, cap / kPage);
+  hipLaunchKernelGGL(pack_kernel, grid, dim3(256), 0, stream, kcache, num_pages, indices, topk_length, s_q, cap, ws);
+  return hipGetLastError();
+}
+
+hipError_t read_and_clear_error_flags(int* flags, hipStream_t stream) {
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return e;
+  int v = 0;
+  e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_error_flags), sizeof(int), 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return e;
+  int zero = 0;
+  e = hipMemcpyToSymbol(HIP_SYMBOL(g_error_flags), &zero, sizeof(int), 0, hipMemcpyHostToDevice);
+  *flags = v;
+  return e;
+}
+
+}  // namespace mla

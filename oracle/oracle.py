@@ -205,12 +205,12 @@ def pack_selected_kv(kcache_rec, indices, topk_length):
 # work went").  The partition rule itself is this library's reading, stated
 # here as a definition:
 #
-#   blocks_r = ceil(max(len_r, 0) / 64), T = sum_r blocks_r.  Concatenate all
-#   requests' blocks in request order; part p (0 <= p < P) owns the global
-#   blocks [floor(p*T/P), floor((p+1)*T/P)).  A request's split count is the
-#   number of parts that own at least one of its blocks; its splits take
-#   consecutive workspace slots in part order, after the slots of all earlier
-#   requests.
+#   blocks_r = ceil(max(len_r, 0) / 64), T = sum_r blocks_r, P' = min(P, T).
+#   Concatenate all requests' blocks in request order; part p < P' owns the
+#   global blocks [floor(p*T/P'), floor((p+1)*T/P')) (at least one block each),
+#   parts p >= P' own nothing.  A request's split count is the number of parts
+#   that own at least one of its blocks; its splits take consecutive workspace
+#   slots in part order, after the slots of all earlier requests.
 
 
 def sched_partition(lengths, num_parts):
@@ -226,8 +226,9 @@ def sched_partition(lengths, num_parts):
     assert P >= 1
     blocks = [(n + PAGE - 1) // PAGE for n in lengths]
     T = sum(blocks)
+    Pe = min(P, T)
     # owner of every global block, found by scanning the part boundaries
-    bounds = [(p * T) // P for p in range(P + 1)]
+    bounds = [(p * T) // Pe for p in range(Pe + 1)] if Pe else [0]
     owner = []
     for g in range(T):
         p = 0

@@ -93,5 +93,6 @@ def pack(kcache_rec, indices, topk_length):
 
 
 def part_of(g, T, P):
-    """Closed form of the owner part of global block g under floor(p*T/P) boundaries."""
-    return ((g + 1) * P - 1) // T
+    """Closed form of the owner part of global block g under floor(p*T/P') boundaries, P' = min(P, T)."""
+    Pe = min(P, T)
+    return ((g + 1) * Pe - 1) // T

@@ -289,6 +289,7 @@ def test_sparse_equals_dense_over_packed_records():
 @pytest.mark.parametrize("lengths,P", [
     ([4096] * 8, 32), ([4096] * 3, 7), ([1, 64, 65, 0, 300], 4), ([0, 0], 3), ([10], 5),
     ([2048, 4096, 3000, 100], 9), ([64] * 5, 5), ([128, 64], 1),
+    ([1, 700, 2049], 64), ([300, 10, 0, 640], 50), ([4096], 256),   # more parts than blocks
 ])
 def test_sched_partition_invariants(lengths, P):
     meta, ns = O.sched_partition(lengths, P)
@@ -312,7 +313,9 @@ def test_sched_partition_invariants(lengths, P):
         assert bs == p - brute.part_of(cum[br], T, P)
     assert np.all(owned == 1)
     if T:
-        assert max(sizes) - min(sizes) <= 1 and sum(sizes) == T
+        Pe = min(P, T)
+        assert all(x > 0 for x in sizes[:Pe]) and all(x == 0 for x in sizes[Pe:])  # empty parts only trail
+        assert max(sizes[:Pe]) - min(sizes[:Pe]) <= 1 and sum(sizes) == T
     for r, nb in enumerate(blocks):
         expect = 0 if nb == 0 else brute.part_of(cum[r] + nb - 1, T, P) - brute.part_of(cum[r], T, P) + 1
         assert ns[r + 1] - ns[r] == expect

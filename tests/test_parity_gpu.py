@@ -1,0 +1,246 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU fp64 oracle.
+
+Tolerances: out |gpu - ref| <= 1e-2 + 1e-2 |ref| element-wise (bf16 output),
+lse |gpu - ref| <= 1e-3 (fp32), plus a relative-RMS alarm at 1e-2 because some
+workloads' output RMS is below the absolute tolerance.  Integer and byte
+results (scheduler records, packed workspace) must match exactly.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from mla_paged_kv_amd import workloads as W
+from oracle import oracle as O
+from tests import gpu_helpers as G
+
+pytestmark = pytest.mark.gpu
+
+ops = pytest.importorskip("mla_paged_kv_amd.ops")
+
+
+def oracle_dense(w):
+    return O.mla_decode(w.q_bits, w.kcache_bits, w.block_table, w.seqlens, w.scale, w.causal)
+
+
+def oracle_sparse(w):
+    return O.mla_sparse_decode(w.q_bits, w.kcache_rec, w.indices, w.seqlens, w.scale)
+
+
+# ----------------------------------------------------------------------------- scheduler
+
+@pytest.mark.parametrize("lengths,P", [
+    ([4096] * 64, 128), ([4096] * 3, 7), ([1, 64, 65, 0, 300], 4), ([0, 0], 3), ([10], 5),
+    ([2048, 4096, 3000, 100], 9), ([64] * 5, 5), ([128, 64], 1), ([16384] * 16, 64),
+    (list(np.random.default_rng(7).integers(0, 5000, size=300)), 200),
+    ([1, 700, 2049], 64), ([300, 10, 0, 640], 50), ([4096], 256),
+])
+def test_sched_metadata_bit_exact(lengths, P):
+    G.say(f"sched lengths[{len(lengths)}] P={P}")
+    seq = torch.tensor(np.asarray(lengths, np.int32), device="cuda:0")
+    meta, ns = ops.mla_get_decode_metadata(seq, len(lengths), 1, 128, 1, P)
+    torch.cuda.synchronize()
+    ref_meta, ref_ns = O.sched_partition(lengths, P)
+    assert np.array_equal(meta.cpu().numpy(), ref_meta)
+    assert np.array_equal(ns.cpu().numpy(), ref_ns)
+
+
+# ----------------------------------------------------------------------------- dense decode
+
+DENSE_SMALL = [
+    # name, seed, batch, s_q, h_q, seqlens, pool_pages, causal, num_parts
+    ("one-page", 101, 1, 1, 16, [64], 2, False, 1),
+    ("ragged-b3-h128", 102, 3, 1, 128, [1, 700, 2049], 60, False, None),
+    ("ragged-b3-h128-p1", 102, 3, 1, 128, [1, 700, 2049], 60, False, 1),
+    ("ragged-b3-h128-p5", 102, 3, 1, 128, [1, 700, 2049], 60, False, 5),
+    ("ragged-b3-h128-p64", 102, 3, 1, 128, [1, 700, 2049], 60, False, 64),
+    ("h16", 103, 2, 1, 16, [333, 64], 8, False, None),
+    ("h32", 104, 2, 1, 32, [333, 65], 8, False, None),
+    ("h48", 105, 2, 1, 48, [31, 500], 10, False, 3),
+    ("h64", 106, 2, 1, 64, [129, 257], 10, False, None),
+    ("h80", 107, 2, 1, 80, [1000, 7], 20, False, 4),
+    ("h112", 108, 1, 1, 112, [777], 13, False, None),
+    ("empty-request", 109, 3, 1, 64, [0, 50, 0], 2, False, None),
+    ("causal-sq2-h128", 110, 3, 2, 128, [1, 100, 1000], 20, True, None),
+    ("causal-sq2-h64-p1", 111, 2, 2, 64, [2, 95], 4, True, 1),
+    ("causal-sq4-h64", 112, 2, 4, 64, [3, 300], 8, True, 6),
+    ("noncausal-sq2-h128", 113, 2, 2, 128, [250, 64], 6, False, None),
+]
+
+
+@pytest.mark.parametrize("case", DENSE_SMALL, ids=[c[0] for c in DENSE_SMALL])
+def test_dense_small(case):
+    name, seed, b, s_q, h_q, seqlens, pool, causal, parts = case
+    G.say(f"dense {name}")
+    w = W.dense_workload(name, seed, b, s_q, h_q, seqlens, pool_pages=pool, causal=causal, num_parts=parts)
+    out, lse, plan = G.run_dense(w)
+    ref = oracle_dense(w)
+    G.compare(name, out, lse, *ref)
+
+
+@pytest.mark.parametrize("cfg", ["c1", "c2"])
+def test_named_small_configs(cfg):
+    G.say(f"config {cfg}")
+    w = W.config(cfg)
+    out, lse, plan = G.run_dense(w)
+    G.say(f"  num_parts={plan.num_parts}")
+    G.compare(cfg, out, lse, *oracle_dense(w))
+
+
+def test_split_invariance_c2():
+    G.say("split invariance c2")
+    w = W.config("c2")
+    ref = oracle_dense(w)
+    t = G.dev_tensors(w)
+    outs = []
+    for parts in (1, 2, 7, 16, 64, 128):
+        out, lse, _ = G.run_dense(w, t, num_parts=parts)
+        G.compare(f"c2-parts{parts}", out, lse, *ref)
+        outs.append(out.float().cpu().numpy())
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) <= 2e-2
+
+
+def test_bitwise_determinism_and_page_permutation():
+    G.say("determinism + page permutation")
+    w = W.dense_workload("perm", 120, 2, 1, 128, [1500, 333], pool_pages=40, num_parts=6)
+    a = G.run_dense(w)
+    b = G.run_dense(w)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    perm = np.random.default_rng(1).permutation(40)
+    inv = np.argsort(perm).astype(np.int32)
+    w2 = G.sub_workload(w, [0, 1])
+    w2.kcache_bits = np.ascontiguousarray(w.kcache_bits[perm])
+    w2.block_table = np.where(w.block_table >= 0, inv[np.maximum(w.block_table, 0)], -1).astype(np.int32)
+    c = G.run_dense(w2)
+    assert torch.equal(a[0], c[0]) and torch.equal(a[1], c[1])
+
+
+def test_nan_in_unreadable_slots_does_not_leak():
+    G.say("NaN sentinel")
+    w = W.dense_workload("nan", 121, 2, 1, 64, [70, 129], pool_pages=6)
+    ref = oracle_dense(w)  # the oracle never reads those slots
+    nan = np.uint16(0x7FC0)
+    used = set()
+    for r in range(2):
+        n = int(w.seqlens[r])
+        for k in range((n + 63) // 64):
+            pg = w.block_table[r, k]
+            used.add(int(pg))
+            if k == (n - 1) // 64:
+                w.kcache_bits[pg, n % 64 or 64:, 0, :] = nan
+    for pg in range(6):
+        if pg not in used:
+            w.kcache_bits[pg] = nan
+    out, lse, _ = G.run_dense(w)
+    G.compare("nan-sentinel", out, lse, *ref)
+
+
+# ----------------------------------------------------------------------------- full-size configurations (sampled rows)
+
+@pytest.mark.parametrize("cfg,sample", [("c3", [0, 17, 63]), ("h", [0, 31, 63]), ("c4", [0, 15])])
+def test_full_size_sampled(cfg, sample):
+    G.say(f"full-size {cfg} sample {sample}")
+    w = W.config(cfg)
+    out, lse, plan = G.run_dense(w)
+    G.say(f"  num_parts={plan.num_parts}")
+    o, l = G.to_np(out, lse)
+    s = G.sub_workload(w, sample)
+    ref = oracle_dense(s)
+    G.compare(f"{cfg}-sampled", o[sample], l[sample], *ref)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+
+
+# ----------------------------------------------------------------------------- combine alone
+
+def test_combine_kernel_against_oracle_partials():
+    G.say("combine isolated")
+    w = W.dense_workload("comb", 130, 3, 1, 32, [300, 0, 190], pool_pages=10, causal=False)
+    # split points per request, as the scheduler would lay them out in slots
+    cuts = {0: [0, 64, 128, 300], 2: [0, 100, 190]}
+    P = 4
+    ns = np.array([0, 3, 3, 5], np.int32)
+    slots = w.batch + P
+    M = w.s_q * w.h_q
+    part_o = np.zeros((slots, M, 512), np.float32)
+    part_l = np.full((slots, M), -np.inf, np.float32)
+    for r, c in cuts.items():
+        for i, (lo, hi) in enumerate(zip(c[:-1], c[1:])):
+            lo_a = np.zeros(w.batch, np.int32)
+            hi_a = np.zeros(w.batch, np.int32)
+            lo_a[r], hi_a[r] = lo, hi
+            po, pl = O.mla_decode_partial(w.q_bits, w.kcache_bits, w.block_table, w.seqlens, w.scale, False, lo_a,
+                                          hi_a)
+            part_o[ns[r] + i] = po[r].reshape(M, 512)
+            part_l[ns[r] + i] = pl[r].reshape(M)
+    ws = np.concatenate([part_o.reshape(-1), part_l.reshape(-1)]).view(np.uint8)
+    ws_t = torch.from_numpy(ws.copy()).cuda()
+    ns_t = torch.from_numpy(ns).cuda()
+    out = torch.full((w.batch, 1, w.h_q, 512), 7.0, dtype=torch.bfloat16, device="cuda:0")
+    lse = torch.full((w.batch, 1, w.h_q), 7.0, dtype=torch.float32, device="cuda:0")
+    ops.mla_combine(ns_t, ws_t, w.batch, 1, w.h_q, P, out, lse)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_dense(w)
+    # request 1 has no split: combine writes 0 / -inf
+    G.compare("combine", out, lse, ref_o, ref_l)
+
+
+# ----------------------------------------------------------------------------- FP8 pack + packed decode
+
+@pytest.mark.parametrize("case", [
+    ("full-tile-h64", 140, 1, 64, 64, [64], 512, 1),
+    ("tails-h64", 141, 3, 64, 192, [192, 65, 1], 4096, 1),
+    ("tails-h128", 142, 2, 128, 256, [100, 256], 2048, 1),
+    ("pack-sq2", 143, 2, 64, 128, [128, 70], 1024, 2),
+], ids=lambda c: c[0])
+def test_pack_bytes_exact(case):
+    name, seed, b, h, cap, topk, ctx, s_q = case
+    G.say(f"pack {name}")
+    w = W.sparse_workload(name, seed, b, h, cap, topk, context=ctx, s_q=s_q)
+    t = G.dev_tensors(w)
+    ws = ops.mla_pack_selected_kv(t["kcache_rec"], t["indices"], t["seqlens"])
+    torch.cuda.synchronize()
+    ref = O.pack_selected_kv(w.kcache_rec, w.indices, w.seqlens)
+    assert np.array_equal(ws.cpu().numpy(), ref.reshape(-1))
+
+
+SPARSE = [
+    ("full-tile-h64", 150, 1, 64, 64, [64], 512, None),
+    ("tails-h64", 151, 3, 64, 192, [192, 65, 1], 4096, None),
+    ("tails-h64-p1", 151, 3, 64, 192, [192, 65, 1], 4096, 1),
+    ("topk2048-h128", 152, 2, 128, 2048, [2048, 2048], 32768, None),
+    ("tails-h128", 153, 3, 128, 512, [400, 17, 512], 8192, 7),
+    ("empty-h64", 154, 2, 64, 128, [0, 77], 1024, None),
+]
+
+
+@pytest.mark.parametrize("case", SPARSE, ids=[c[0] for c in SPARSE])
+def test_fp8_packed_decode(case):
+    name, seed, b, h, cap, topk, ctx, parts = case
+    G.say(f"fp8 {name}")
+    w = W.sparse_workload(name, seed, b, h, cap, topk, context=ctx, num_parts=parts)
+    out, lse, ws, plan = G.run_sparse(w)
+    G.compare(name, out, lse, *oracle_sparse(w))
+
+
+def test_config_c5():
+    G.say("config c5")
+    w = W.config("c5")
+    out, lse, ws, plan = G.run_sparse(w)
+    G.say(f"  num_parts={plan.num_parts}")
+    ref_ws = O.pack_selected_kv(w.kcache_rec, w.indices, w.seqlens)
+    assert np.array_equal(ws.cpu().numpy(), ref_ws.reshape(-1))
+    G.compare("c5", out, lse, *oracle_sparse(w))
+
+
+# ----------------------------------------------------------------------------- device-side contract checks
+
+def test_out_of_range_page_sets_flag_without_fault():
+    G.say("device flag: page out of range")
+    ops.mla_read_device_errors()  # clear
+    w = W.dense_workload("badpage", 160, 1, 1, 16, [100], pool_pages=2)
+    w.block_table[0, 1] = 99  # the kernel must not read page 99; it clamps and flags
+    G.run_dense(w)
+    flags = ops.mla_read_device_errors()
+    assert flags & 1
+    assert ops.mla_read_device_errors() == 0
