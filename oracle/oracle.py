@@ -83,11 +83,15 @@ def _load():
     return _lib
 
 
+MAX_THREADS = 16  # the CPU share of one GPU on the machines this runs on
+
+
 def default_threads() -> int:
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return max(1, os.cpu_count() or 1)
+        n = os.cpu_count() or 1
+    return max(1, min(n, MAX_THREADS))
 
 
 def _ptr(a: np.ndarray):
