@@ -99,8 +99,14 @@ __device__ __forceinline__ void sync_lds() {
   asm volatile("" ::: "memory");
 }
 
+// global_load_lds_dwordx4: lane i writes its 16 source bytes to LDS at M0 + 16*i.
+// Issued through inline asm on purpose: the compiler then knows of no pending
+// LDS DMA, so it inserts no vmcnt(0) in front of later LDS reads (it cannot
+// tell they touch other ring slots).  The ring's completion is tracked with the
+// explicit wait_vmcnt calls instead.  Nothing else in these kernels uses M0.
 __device__ __forceinline__ void load_lds16(const void* gsrc, LDS_AS void* ldst) {
-  __builtin_amdgcn_global_load_lds(gsrc, ldst, 16, 0, 0);
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)ldst);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(m0v) : "memory");
 }
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const LDS_AS uint8_t* p) {
@@ -109,18 +115,9 @@ __device__ __forceinline__ bf16x8 lds_read_b128(const LDS_AS uint8_t* p) {
 
 // Transposed 4 x 16 read (ds_read_b64_tr_b16): in each 16-lane group, lanes
 // 4r..4r+3 address the 16 consecutive bf16 of row r (4 each); lane i receives
-// column i of rows 0..3.  Issued through inline asm: the compiler does not know
-// this intrinsic cannot alias the in-flight global->LDS loads and would
-// otherwise put a vmcnt(0) in front of it.  The caller must call
-// lds_wait_tr16() on the result before using it.
-__device__ __forceinline__ u32x2 lds_read_tr16(const LDS_AS uint8_t* p) {
-  u32x2 r;
-  const uint32_t addr = (uint32_t)(uintptr_t)p;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr) : "memory");
-  return r;
-}
-__device__ __forceinline__ void lds_wait_tr16(u32x2& a, u32x2& b) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b)::"memory");
+// column i of rows 0..3.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const LDS_AS uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(reinterpret_cast<LDS_AS bf16x4*>(const_cast<LDS_AS uint8_t*>(p)));
 }
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -133,8 +130,37 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
-__device__ __forceinline__ float wave_xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
-__device__ __forceinline__ float wave_xor_sum(float v, int mask) { return v + __shfl_xor(v, mask, 64); }
+// A score row lives in lanes l, l^16, l^32, l^48.  v_permlane16_swap /
+// v_permlane32_swap exchange half-rows between two registers; with both holding
+// x, the pair that comes back is {x[l], x[l^16]} (resp. x[l^32]), so two VALU
+// ops reduce a row without a trip through LDS.  Inline asm on purpose: with
+// both operands equal, the compiler's builtin folds the returned pair to a single
+// value (observed: the max of the pair disappeared).  The s_nop covers the
+// VALU-write -> permlane-read hazard.
+__device__ __forceinline__ void permlane_pair16(float& a, float& b) {
+  asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void permlane_pair32(float& a, float& b) {
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float row4_max(float v) {
+  float a = v, b = v;
+  permlane_pair16(a, b);
+  v = fmaxf(a, b);
+  a = v;
+  b = v;
+  permlane_pair32(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float row4_sum(float v) {
+  float a = v, b = v;
+  permlane_pair16(a, b);
+  v = a + b;
+  a = v;
+  b = v;
+  permlane_pair32(a, b);
+  return a + b;
+}
 
 // byte offset of (key row kr, 16-B chunk c) inside a swizzled bf16 tile
 __device__ __forceinline__ uint32_t tile_off(int kr, int c) {
@@ -515,8 +541,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
             sv[kb * 4 + i] = key0 + kr < lim ? x : -INFINITY;
             mx = fmaxf(mx, sv[kb * 4 + i]);
           }
-        mx = wave_xor_max(mx, 16);
-        mx = wave_xor_max(mx, 32);
+        mx = row4_max(mx);
         const float mold = mrow;
         const bool upd = mx > mold + kRescaleThreshold;
         const float mnew = upd ? mx : mold;
@@ -567,31 +592,20 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
       const int kr0 = 8 * g + tr_r;
       const uint32_t within = (tr_j & 1) * 8;
       // V^T operand of dim block db (16 columns): keys 8g..8g+7 of column 128w+16db+li
-      auto vt_issue = [&](int db, u32x2& v0, u32x2& v1) {
-        const int c = 16 * w + 2 * db + (tr_j >> 1);  // chunk holding dims 128w + 16db + 4j ..
-        v0 = lds_read_tr16(kt + tile_off(kr0, c) + within);
-        v1 = lds_read_tr16(kt + tile_off(kr0 + 4, c) + within);
-      };
-      u32x2 c0, c1;
-      vt_issue(0, c0, c1);
-      lds_wait_tr16(c0, c1);
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        u32x2 n0 = c0, n1 = c1;
-        if (db + 1 < 8) vt_issue(db + 1, n0, n1);
-        const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{c0.x, c0.y, c1.x, c1.y});
+        const int c = 16 * w + 2 * db + (tr_j >> 1);  // chunk holding dims 128w + 16db + 4j ..
+        const bf16x4 v0 = lds_read_tr16(kt + tile_off(kr0, c) + within);
+        const bf16x4 v1 = lds_read_tr16(kt + tile_off(kr0 + 4, c) + within);
+        const bf16x8 av = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) o[db][rb] = mfma16(av, bp[rb], o[db][rb]);
-        if (db + 1 < 8) lds_wait_tr16(n0, n1);
-        c0 = n0;
-        c1 = n1;
       }
     }
 
     // ---- epilogue: row sums to LDS, then normalise and store
     if (qk_wave) {
-      float lt = wave_xor_sum(lpart, 16);
-      lt = wave_xor_sum(lt, 32);
+      const float lt = row4_sum(lpart);
       if (g == 0) {
         l_s[row_local] = lt;
         if (rho < a.M) {
@@ -629,6 +643,285 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
   }
 }
 
+// ------------------------------------------------------------------ dense decode, software-pipelined
+//
+// Same work split as decode_kernel, with one barrier per 32-key tile and the
+// tile loop skewed by one stage: iteration t issues the LDS reads of PV(t-1)'s
+// operands, runs QK^T(t) (whose 36 MFMAs hide those reads), then PV(t-1)'s 32
+// MFMAs in the same basic block as softmax(t) so that the VALU softmax work
+// issues while the MFMA pipe is busy.  P, the rescale factors and their flags
+// are double-buffered; the K ring keeps tiles t-1 (PV), t (QK), t+1 and t+2
+// (in flight), and tile t+3 is issued after the barrier that ends iteration t.
+constexpr int kLPW = kLoadsPerWave;
+constexpr int kDOffP = kStages * kTileBytes;                  // 147456
+constexpr int kDOffAlpha = kDOffP + 2 * kPBufBytes;           // 157696
+constexpr int kDOffFlag = kDOffAlpha + 2 * kMaxRowsPerWG * 4; // 158208
+constexpr int kDOffL = kDOffFlag + 64;                        // 158272
+constexpr int kDLdsBytes = kDOffL + kMaxRowsPerWG * 4;        // 158528
+static_assert(kDLdsBytes <= 160 * 1024, "dense pipelined LDS budget");
+
+// S^T (32 keys x 16 rows) = K Q^T over 576 dims: 18 k-steps x 2 key blocks,
+// LDS operand reads issued two k-steps ahead.
+__device__ __forceinline__ void qk_tile(const LDS_AS uint8_t* kt, uint32_t base0, uint32_t base1,
+                                        const bf16x8 (&qreg)[18], f32x4 (&acc)[2]) {
+  auto addr = [&](int s) { return ((s & 1) ? base1 : base0) + (uint32_t)((s >> 1) * 128); };
+  bf16x8 k0[3], k1[3];
+  k0[0] = lds_read_b128(kt + addr(0));
+  k1[0] = lds_read_b128(kt + addr(0) + 16 * kRowBytes);
+  k0[1] = lds_read_b128(kt + addr(1));
+  k1[1] = lds_read_b128(kt + addr(1) + 16 * kRowBytes);
+  acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 18; ++s) {
+    if (s + 2 < 18) {
+      k0[(s + 2) % 3] = lds_read_b128(kt + addr(s + 2));
+      k1[(s + 2) % 3] = lds_read_b128(kt + addr(s + 2) + 16 * kRowBytes);
+    }
+    acc[0] = mfma16(k0[s % 3], qreg[s], acc[0]);
+    acc[1] = mfma16(k1[s % 3], qreg[s], acc[1]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int RB>
+__global__ __launch_bounds__(kDecodeThreads, 1) void decode_dense_kernel(DecodeArgs a) {
+  constexpr int MB = 16 * RB;
+  constexpr bool kAllQK = RB == 4;  // every wave owns a 16-row block of scores
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[kDLdsBytes];
+  LDS_AS uint8_t* smem = (LDS_AS uint8_t*)(smem_raw);  // C-style: generic -> LDS address space
+  LDS_AS float* alpha_s = reinterpret_cast<LDS_AS float*>(smem + kDOffAlpha);  // [2][64]
+  LDS_AS int* flag_s = reinterpret_cast<LDS_AS int*>(smem + kDOffFlag);        // [2][4]
+  LDS_AS float* l_s = reinterpret_cast<LDS_AS float*>(smem + kDOffL);
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, g = l >> 4, li = l & 15;
+  const bool qk_wave = kAllQK || w < RB;
+  const int part = blockIdx.x, rbk = blockIdx.y;
+  const int begin_req = ld_const(a.sched_meta, part * 8 + 0);
+  if (begin_req < 0) return;
+  const int begin_blk = ld_const(a.sched_meta, part * 8 + 1);
+  const int end_req = ld_const(a.sched_meta, part * 8 + 2);
+  const int end_blk = ld_const(a.sched_meta, part * 8 + 3);
+  const int begin_split = ld_const(a.sched_meta, part * 8 + 4);
+  if (begin_req >= a.batch || end_req >= a.batch || end_req < begin_req) {  // not a scheduler record
+    if (threadIdx.x == 0) atomicOr(&g_error_flags, kErrMeta);
+    return;
+  }
+
+  TileLoader<false> loader;
+  loader.init(w, l);
+  const int kx = li & 7;
+  const uint32_t kq_base0 = (uint32_t)(li * kRowBytes + 16 * (4 * (0 ^ (kx >> 2)) + (g ^ (kx & 3))));
+  const uint32_t kq_base1 = (uint32_t)(li * kRowBytes + 16 * (4 * (1 ^ (kx >> 2)) + (g ^ (kx & 3))));
+  const int kr0 = 8 * g + (li >> 2);        // transposed V read: key row of this lane (and +4)
+  const int tr_j = li & 3;
+  const uint32_t tr_within = (tr_j & 1) * 8;
+  const int row_local = 16 * w + li;
+
+  for (int r = begin_req; r <= end_req; ++r) {
+    int seqlen = ld_const(a.seqlens, r);
+    if (seqlen < 0 || seqlen > a.max_pages * kPage) {
+      if (tid == 0) atomicOr(&g_error_flags, kErrSeqlen);
+      seqlen = seqlen < 0 ? 0 : a.max_pages * kPage;
+    }
+    const int nblk = (seqlen + kPage - 1) / kPage;
+    const int blk0 = (r == begin_req) ? begin_blk : 0;
+    const int blk1 = (r == end_req) ? end_blk : nblk;
+    const int t0 = blk0 * kPage;
+    const int t1 = min(blk1 * kPage, seqlen);
+    const int ntile = t1 > t0 ? (t1 - t0 + kTK - 1) / kTK : 0;
+    const int split = (r == begin_req) ? begin_split : 0;
+    const int ns0 = ld_const(a.num_splits, r);
+    const int nsplit = ld_const(a.num_splits, r + 1) - ns0;
+    const int slot = ns0 + split;
+    if (nsplit > 1 && (slot < 0 || slot >= a.slots)) {  // inconsistent metadata: skip, never write out of range
+      if (threadIdx.x == 0) atomicOr(&g_error_flags, kErrMeta);
+      continue;
+    }
+
+    const int rho = rbk * MB + row_local;
+    const bool live = qk_wave && rho < a.M;
+    bf16x8 qreg[18];
+    {
+      const uint16_t* qrow = a.q + ((int64_t)r * a.M + (live ? rho : 0)) * kDQK + 8 * g;
+#pragma unroll
+      for (int s = 0; s < 18; ++s) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 32 * s);
+        qreg[s] = live ? v : bf16x8{};
+      }
+    }
+    int lim = 0;
+    if (live) {
+      int nvis = seqlen;
+      if (a.causal) nvis = min(max(seqlen - a.s_q + rho / a.h_q + 1, 0), seqlen);
+      lim = min(t1, nvis);
+    }
+    float mrow = -INFINITY, lpart = 0.f;
+    f32x4 o[8][RB];
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int tt = 0; tt < kStages - 1; ++tt)
+      if (tt < ntile) loader.issue(a, r, t0 + tt * kTK, smem, tt, w);
+
+    // softmax of tile t: scores in acc -> P (bf16) into P buffer t&1, rescale factor and flag
+    auto softmax = [&](int t, const f32x4 (&acc)[2]) {
+      const int key0 = t0 + t * kTK;
+      float sv[8];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = acc[kb][i] * a.scale_log2;
+          sv[kb * 4 + i] = key0 + 16 * kb + 4 * g + i < lim ? x : -INFINITY;
+          mx = fmaxf(mx, sv[kb * 4 + i]);
+        }
+      mx = row4_max(mx);
+      const float mold = mrow;
+      const bool upd = mx > mold + kRescaleThreshold;
+      const float mnew = upd ? mx : mold;
+      const float alpha = upd ? fast_exp2(mold - mnew) : 1.f;
+      mrow = mnew;
+      const float mref = (mnew == -INFINITY) ? 0.f : mnew;
+      float pv[8];
+      float psum = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        pv[k] = fast_exp2(sv[k] - mref);
+        psum += pv[k];
+      }
+      lpart = lpart * alpha + psum;
+      LDS_AS uint8_t* prow = smem + kDOffP + (t & 1) * kPBufBytes + row_local * kPStride + 8 * g;
+      *reinterpret_cast<LDS_AS u32x2*>(prow) = u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
+      *reinterpret_cast<LDS_AS u32x2*>(prow + 32) = u32x2{pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
+      if (g == 0) alpha_s[(t & 1) * kMaxRowsPerWG + row_local] = alpha;
+      const bool any = __any(upd);
+      if (l == 0) flag_s[(t & 1) * 4 + w] = any ? 1 : 0;
+    };
+
+    // operands of PV(t): P^T rows of every row block, V^T of the wave's 8 column blocks
+    struct PvOps {
+      bf16x8 bp[RB];
+      bf16x4 v[8][2];
+    };
+    auto pv_issue = [&](int t, PvOps& op) {
+      const LDS_AS uint8_t* pb = smem + kDOffP + (t & 1) * kPBufBytes;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) op.bp[rb] = lds_read_b128(pb + (16 * rb + li) * kPStride + 16 * g);
+      const LDS_AS uint8_t* kt = smem + kOffKDense + (t & 3) * kTileBytes;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const int c = 16 * w + 2 * db + (tr_j >> 1);
+        op.v[db][0] = lds_read_tr16(kt + tile_off(kr0, c) + tr_within);
+        op.v[db][1] = lds_read_tr16(kt + tile_off(kr0 + 4, c) + tr_within);
+      }
+    };
+    auto pv_finish = [&](int t, PvOps& op) {
+      if (t > 0) {  // O is still zero before the first tile: nothing to rescale
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          if (flag_s[(t & 1) * 4 + rb]) {
+            const float al = alpha_s[(t & 1) * kMaxRowsPerWG + 16 * rb + li];
+#pragma unroll
+            for (int db = 0; db < 8; ++db) o[db][rb] *= al;
+          }
+        }
+      }
+    };
+    auto pv_mfma = [&](PvOps& op) {
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const bf16x8 av = __builtin_shufflevector(op.v[db][0], op.v[db][1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) o[db][rb] = mfma16(av, op.bp[rb], o[db][rb]);
+      }
+    };
+    // end of iteration t: tile t+1 resident and visible, P(t) visible, ring slot of t-1 refilled
+    auto advance = [&](int t) {
+      if (t + 1 < ntile) {
+        if (t + 2 < ntile) wait_vmcnt<kLPW>();
+        else wait_vmcnt<0>();
+      }
+      sync_lds();
+      if (t + 3 < ntile) loader.issue(a, r, t0 + (t + 3) * kTK, smem, (t + 3) & 3, w);
+    };
+    auto tail_fixup = [&](int t) {
+      const int nvalid = min(kTK, t1 - (t0 + t * kTK));
+      if (nvalid < kTK) zero_tail_rows(smem + kOffKDense + (t & 3) * kTileBytes, nvalid);
+    };
+
+    if (ntile > 0) {
+      if (ntile > 2) wait_vmcnt<2 * kLPW>();
+      else if (ntile > 1) wait_vmcnt<kLPW>();
+      else wait_vmcnt<0>();
+      sync_lds();
+      // iteration 0: QK^T and softmax only
+      tail_fixup(0);
+      if (qk_wave) {
+        f32x4 acc[2];
+        qk_tile(smem + kOffKDense, kq_base0, kq_base1, qreg, acc);
+        softmax(0, acc);
+      }
+      advance(0);
+      for (int t = 1; t < ntile; ++t) {
+        tail_fixup(t);
+        PvOps op;
+        pv_issue(t - 1, op);
+        f32x4 acc[2];
+        if (qk_wave) qk_tile(smem + kOffKDense + (t & 3) * kTileBytes, kq_base0, kq_base1, qreg, acc);
+        pv_finish(t - 1, op);
+        pv_mfma(op);
+        if (qk_wave) softmax(t, acc);
+        advance(t);
+      }
+      PvOps op;
+      pv_issue(ntile - 1, op);
+      pv_finish(ntile - 1, op);
+      pv_mfma(op);
+    }
+
+    // ---- epilogue: row sums to LDS, then normalise and store
+    if (qk_wave) {
+      const float lt = row4_sum(lpart);
+      if (g == 0) {
+        l_s[row_local] = lt;
+        if (rho < a.M) {
+          const float lse = lt > 0.f ? (mrow + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
+          if (nsplit == 1) a.lse[(int64_t)r * a.M + rho] = lse;
+          else a.part_lse[(int64_t)slot * a.M + rho] = lse;
+        }
+      }
+    }
+    sync_lds();
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int rho_o = rbk * MB + 16 * rb + li;
+      if (rho_o >= a.M) continue;
+      const float lt = l_s[16 * rb + li];
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      if (nsplit == 1) {
+        uint16_t* orow = a.out + ((int64_t)r * a.M + rho_o) * kDV + 128 * w + 4 * g;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const f32x4 v = o[db][rb] * inv;
+          *reinterpret_cast<u32x2*>(orow + 16 * db) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        }
+      } else {
+        float* prow = a.part_o + ((int64_t)slot * a.M + rho_o) * kDV + 128 * w + 4 * g;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(prow + 16 * db) = o[db][rb] * inv;
+      }
+    }
+    wait_vmcnt<0>();
+    sync_lds();
+  }
+}
+
 // 16-row blocks per workgroup.  Capped at 4 (64 rows): at 128 rows the Q and O
 // register tiles alone take ~400 of a wave's 512 registers and the compiler
 // spills; an h_q = 128 request is covered by two 64-row workgroups whose
@@ -644,7 +937,10 @@ template <int RB, bool FP8>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   const int MB = 16 * RB;
   dim3 grid(a.num_parts, (a.M + MB - 1) / MB);
-  hipLaunchKernelGGL((decode_kernel<RB, FP8>), grid, dim3(kDecodeThreads), 0, stream, a);
+  if constexpr (FP8)
+    hipLaunchKernelGGL((decode_kernel<RB, true>), grid, dim3(kDecodeThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_dense_kernel<RB>), grid, dim3(kDecodeThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -661,13 +957,13 @@ hipError_t decode_occupancy(bool fp8, int M, int* wgs_per_cu) {
   hipError_t e;
   switch (decode_row_blocks_per_wg(M)) {
     case 1: e = fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<1, true>, kDecodeThreads, 0)
-                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<1, false>, kDecodeThreads, 0);
+                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_dense_kernel<1>, kDecodeThreads, 0);
       break;
     case 2: e = fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<2, true>, kDecodeThreads, 0)
-                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<2, false>, kDecodeThreads, 0);
+                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_dense_kernel<2>, kDecodeThreads, 0);
       break;
     default: e = fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<4, true>, kDecodeThreads, 0)
-                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<4, false>, kDecodeThreads, 0);
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_dense_kernel<4>, kDecodeThreads, 0);
       break;
   }
   *wgs_per_cu = n;
