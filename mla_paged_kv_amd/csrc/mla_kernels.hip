@@ -31,6 +31,8 @@
 //     same swizzled bf16 tile the dense path uses.
 #include "mla_internal.h"
 
+#include <type_traits>
+
 #include <math.h>
 
 namespace mla {
@@ -44,6 +46,24 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 
 __device__ int g_error_flags;
+
+// Phase-timing hooks for the wave-specialised kernel.  They expand to nothing
+// unless MLA_PROFILE is defined (a profiling build reads the per-wave sums of
+// s_memtime deltas through mla_debug_read_prof).
+#ifdef MLA_PROFILE
+__device__ unsigned long long g_prof[4096 * 16];
+#define MLA_PROF_DECL unsigned long long prof_acc_[8] = {}, prof_tiles_ = 0; unsigned prof_last_ = (unsigned)__builtin_amdgcn_s_memtime();
+#define MLA_PROF_RESET prof_last_ = (unsigned)__builtin_amdgcn_s_memtime();
+#define MLA_PROF(i) do { unsigned c_ = (unsigned)__builtin_amdgcn_s_memtime(); prof_acc_[i] += (unsigned)(c_ - prof_last_); prof_last_ = c_; } while (0)
+#define MLA_PROF_TILES(n) prof_tiles_ += (n);
+#define MLA_PROF_DUMP(slot) if ((threadIdx.x & 63) == 0) { for (int i_ = 0; i_ < 8; ++i_) g_prof[(slot) * 16 + i_] = prof_acc_[i_]; g_prof[(slot) * 16 + 15] = prof_tiles_; }
+#else
+#define MLA_PROF_DECL
+#define MLA_PROF_RESET
+#define MLA_PROF(i)
+#define MLA_PROF_TILES(n)
+#define MLA_PROF_DUMP(slot)
+#endif
 
 // Read-only kernel inputs that every lane of a wave indexes the same way (page
 // table, lengths, scheduler records) are read through the constant address
@@ -64,14 +84,16 @@ constexpr int kRowBytes = kDQK * 2;                 // 1152
 constexpr int kTileBytes = kTK * kRowBytes;         // 36864
 constexpr int kChunksPerRow = kRowBytes / 16;       // 72
 constexpr int kLoadsPerWave = kTileBytes / 1024 / 4;  // 9 wave-wide 16-B loads per tile per wave
-constexpr int kPStride = kTK * 2 + 16;              // P row pitch (bytes), padded against bank conflicts
+// P row pitch (bytes).  Measured on gfx950: 16-B reads of 16 rows at a 64-, 80-
+// or 144-B pitch run at half rate (bank conflicts), at 96 B at full rate.
+constexpr int kPStride = kTK * 2 + 32;
 constexpr int kRawTileBytes = 24 * 1024;            // FP8 raw tile slot (32 x 656 = 20992 B used)
 constexpr int kRawLoadsPerWave = 6;                 // 24 wave-wide loads per raw tile
 constexpr int kRawChunks = kTK * kRecBytes / 16;    // 1312
 constexpr float kRescaleThreshold = 8.0f;           // log2 units: p <= 2^8 between rescales
 
 // LDS layout
-constexpr int kPBufBytes = kMaxRowsPerWG * kPStride;            // one P buffer (5 KB)
+constexpr int kPBufBytes = kMaxRowsPerWG * kPStride;            // one P buffer (6 KB)
 constexpr int kOffKDense = 0;
 constexpr int kOffRaw = 0;                                      // FP8: raw ring
 constexpr int kOffKFp8 = kStages * kRawTileBytes;               // FP8: widened bf16 tile
@@ -107,6 +129,20 @@ __device__ __forceinline__ void sync_lds() {
 __device__ __forceinline__ void load_lds16(const void* gsrc, LDS_AS void* ldst) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)ldst);
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(m0v) : "memory");
+}
+
+// Same, with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane offset
+// (saddr form): no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void load_lds16_s(const void* sbase, uint32_t voff, LDS_AS void* ldst) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)ldst);
+  // the base is wave-uniform by contract; readfirstlane makes that visible so
+  // that it is allocated to SGPRs.  The builtin returns a signed int: each half
+  // goes through uint32_t so that the low word is zero-extended, not sign-extended.
+  const uint64_t b = (uint64_t)(uintptr_t)sbase;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint64_t bu = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(bu), "s"(m0v) : "memory");
 }
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const LDS_AS uint8_t* p) {
@@ -276,29 +312,45 @@ struct TileLoader;
 // bf16 pages: tile = 32 consecutive keys of one 64-token page (36,864 contiguous bytes).
 template <>
 struct TileLoader<false> {
-  uint32_t off[kLoadsPerWave];  // per-lane source offset inside the tile for each of this wave's loads
+  // Load qi = w + 4k (k < 9) of a tile fills LDS chunks [64qi, 64qi+64); lane
+  // l's chunk lies in key row kr = (64qi + l) / 72, and (72 being a multiple of
+  // 8) its swizzled source offset in the tile is 1024qi + 16((l & 56) |
+  // ((l ^ kr) & 7)).  The three lane-dependent bits of the nine loads share one
+  // register; the 1024qi part goes into the wave-uniform base.
+  uint32_t bits, l56;
   __device__ void init(int w, int l) {
+    bits = 0;
+    l56 = 16u * (uint32_t)(l & 56);
 #pragma unroll
     for (int k = 0; k < kLoadsPerWave; ++k) {
-      int qi = w + 4 * k;           // wave-wide load index within the tile (0..35)
-      int p = qi * 64 + l;          // destination 16-B chunk position in the tile
-      int kr = p / kChunksPerRow;
-      int pos = p - kr * kChunksPerRow;
-      int c = pos ^ (kr & 7);       // logical chunk stored at that position
-      off[k] = (uint32_t)(kr * kRowBytes + c * 16);
+      const int qi = w + 4 * k;
+      const int kr = (qi * 64 + l) / kChunksPerRow;
+      bits |= (uint32_t)((l ^ kr) & 7) << (3 * k);
     }
   }
   // Issues this wave's loads of tile `tile` of request r into stage `st`.
   __device__ void issue(const DecodeArgs& a, int r, int key0, LDS_AS uint8_t* smem, int st, int w) {
-    int64_t page = ld_const(a.block_table, (int64_t)r * a.max_pages + (key0 >> 6));
+    issue_page(a, ld_const(a.block_table, (int64_t)r * a.max_pages + (key0 >> 6)), key0, smem, st, w);
+  }
+  // Same, with the page id already looked up (wave-uniform).
+  __device__ void issue_page(const DecodeArgs& a, int64_t page, int key0, LDS_AS uint8_t* smem, int st, int w) {
+    const uint8_t* src = tile_src(a, page, key0);
+#pragma unroll
+    for (int k = 0; k < kLoadsPerWave; ++k) issue_one(src, smem, st, w, k);
+  }
+  // Base addresses of tile (page, key0) for issue_one.
+  __device__ const uint8_t* tile_src(const DecodeArgs& a, int64_t page, int key0) const {
     if (page < 0 || page >= a.num_pages) {
       if ((threadIdx.x & 63) == 0) atomicOr(&g_error_flags, kErrPage);
       page = 0;  // stay in bounds; the output of this request is undefined
     }
-    const uint8_t* src = a.kv + page * (int64_t)(kPage * kRowBytes) + (key0 & 63) * kRowBytes;
-    LDS_AS uint8_t* dst = smem + kOffKDense + st * kTileBytes;
-#pragma unroll
-    for (int k = 0; k < kLoadsPerWave; ++k) load_lds16(src + off[k], dst + (w + 4 * k) * 1024);
+    return a.kv + page * (int64_t)(kPage * kRowBytes) + (key0 & 63) * kRowBytes;
+  }
+  // The k-th of this wave's kLoadsPerWave loads of a tile.
+  __device__ void issue_one(const uint8_t* src, LDS_AS uint8_t* smem, int st, int w, int k) const {
+    const int qi = w + 4 * k;
+    const uint32_t voff = l56 + 16u * ((bits >> (3 * k)) & 7u);
+    load_lds16_s(src + qi * 1024, voff, smem + kOffKDense + st * kTileBytes + qi * 1024);
   }
 };
 
@@ -362,8 +414,11 @@ __device__ __forceinline__ void zero_tail_rows(LDS_AS uint8_t* kt, int nvalid) {
   }
 }
 
+// one v_cvt_pk_bf16_f32 (round to nearest even), a in the low half
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
 }
 
 // One workgroup: the 16*RB query rows of row block blockIdx.y, over the KV range
@@ -643,60 +698,101 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
   }
 }
 
-// ------------------------------------------------------------------ dense decode, software-pipelined
+// ------------------------------------------------------------------ dense decode: LDS layout
 //
-// Same work split as decode_kernel, with one barrier per 32-key tile and the
-// tile loop skewed by one stage: iteration t issues the LDS reads of PV(t-1)'s
-// operands, runs QK^T(t) (whose 36 MFMAs hide those reads), then PV(t-1)'s 32
-// MFMAs in the same basic block as softmax(t) so that the VALU softmax work
-// issues while the MFMA pipe is busy.  P, the rescale factors and their flags
-// are double-buffered; the K ring keeps tiles t-1 (PV), t (QK), t+1 and t+2
-// (in flight), and tile t+3 is issued after the barrier that ends iteration t.
+// A ring of kStages 32-key tiles (tile t in slot t & 3), double-buffered P
+// (bf16, 64 rows x 32 keys, padded rows), per-row rescale factors and per-row-
+// block flags, the row sums handed to the output stage, and the page ids of
+// the request piece being processed.
 constexpr int kLPW = kLoadsPerWave;
 constexpr int kDOffP = kStages * kTileBytes;                  // 147456
-constexpr int kDOffAlpha = kDOffP + 2 * kPBufBytes;           // 157696
-constexpr int kDOffFlag = kDOffAlpha + 2 * kMaxRowsPerWG * 4; // 158208
-constexpr int kDOffL = kDOffFlag + 64;                        // 158272
-constexpr int kDLdsBytes = kDOffL + kMaxRowsPerWG * 4;        // 158528
+constexpr int kDOffAlpha = kDOffP + 2 * kPBufBytes;           // 159744
+constexpr int kDOffFlag = kDOffAlpha + 2 * kMaxRowsPerWG * 4; // 160256
+constexpr int kDOffL = kDOffFlag + 64;                        // 160320
+constexpr int kPageCache = 512;                               // page ids cached per request piece
+constexpr int kDOffPages = kDOffL + kMaxRowsPerWG * 4;        // 160576
+constexpr int kDLdsBytes = kDOffPages + kPageCache * 4;       // 162624
 static_assert(kDLdsBytes <= 160 * 1024, "dense pipelined LDS budget");
 
-// S^T (32 keys x 16 rows) = K Q^T over 576 dims: 18 k-steps x 2 key blocks,
-// LDS operand reads issued two k-steps ahead.
+// S^T (32 keys x 16 rows) = K Q^T over 576 dims: 18 k-steps x 2 key blocks.
+// The K operands come from LDS through a ring of D fragments per key block, so
+// the reads of k-step s+D-1 are in flight while the MFMAs of k-step s run.
+struct NoHook {
+  __device__ void operator()(int) const {}
+};
+
+template <int D, class Hook = NoHook>
 __device__ __forceinline__ void qk_tile(const LDS_AS uint8_t* kt, uint32_t base0, uint32_t base1,
-                                        const bf16x8 (&qreg)[18], f32x4 (&acc)[2]) {
+                                        const bf16x8 (&qreg)[18], f32x4 (&acc)[2], const Hook& hook = Hook()) {
+  static_assert(D >= 2 && D <= 8, "K operand ring depth");
   auto addr = [&](int s) { return ((s & 1) ? base1 : base0) + (uint32_t)((s >> 1) * 128); };
-  bf16x8 k0[3], k1[3];
-  k0[0] = lds_read_b128(kt + addr(0));
-  k1[0] = lds_read_b128(kt + addr(0) + 16 * kRowBytes);
-  k0[1] = lds_read_b128(kt + addr(1));
-  k1[1] = lds_read_b128(kt + addr(1) + 16 * kRowBytes);
+  bf16x8 k0[D], k1[D];
+#pragma unroll
+  for (int s = 0; s < D - 1; ++s) {
+    k0[s] = lds_read_b128(kt + addr(s));
+    k1[s] = lds_read_b128(kt + addr(s) + 16 * kRowBytes);
+  }
   acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < 18; ++s) {
-    if (s + 2 < 18) {
-      k0[(s + 2) % 3] = lds_read_b128(kt + addr(s + 2));
-      k1[(s + 2) % 3] = lds_read_b128(kt + addr(s + 2) + 16 * kRowBytes);
+    if (s + D - 1 < 18) {
+      k0[(s + D - 1) % D] = lds_read_b128(kt + addr(s + D - 1));
+      k1[(s + D - 1) % D] = lds_read_b128(kt + addr(s + D - 1) + 16 * kRowBytes);
     }
-    acc[0] = mfma16(k0[s % 3], qreg[s], acc[0]);
-    acc[1] = mfma16(k1[s % 3], qreg[s], acc[1]);
+    acc[0] = mfma16(k0[s % D], qreg[s], acc[0]);
+    acc[1] = mfma16(k1[s % D], qreg[s], acc[1]);
+    hook(s);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
+// ------------------------------------------------------------------ dense decode, wave-specialised
+//
+// 8 waves, two per SIMD with different jobs, so that one wave's MFMAs fill the
+// pipe while the other waits on LDS or runs VALU work:
+//   * QK waves 0..3: wave w holds Q for rows [16w, 16w+16) in registers.  In
+//     iteration t it computes S(t)^T = K(t) Q^T and, between those MFMAs, the
+//     online softmax of S(t-1) (kept in registers from the previous iteration),
+//     writing P(t-1) (bf16), the rescale factor and a flag to double-buffered
+//     LDS slots.  The VALU softmax thus runs in the shadow of the MFMAs.
+//   * PV waves 4..7: wave 4+w owns output columns [128w, 128w+128) for all rows
+//     (O in registers).  In iteration t it computes O += V(t-2)^T P(t-2)^T with
+//     V(t-2) held in registers and, after each 16-column block, reads the same
+//     block of V(t-1) from the ring into the freed registers.  It also streams
+//     the ring: tile t+2 goes into the slot of tile t-2 (whose K and V were read
+//     in iterations t-2 and t-1).
+// One barrier per 32-key tile ends iteration t: after it tile t+1 is resident,
+// P(t-1) is visible, and the V(t-1) reads of every PV wave have completed.  The
+// loop runs two extra iterations to drain the softmax and PV stages.
+constexpr int kWsThreads = 512;
+constexpr int kQkDepth = 5;  // K operand ring depth of the QK waves (they have registers to spare)
+
+// Zero V rows [nvalid, 32) of a bf16 tile; `tid` in [0, 256) strides by 256.
+__device__ __forceinline__ void zero_tail_rows_256(LDS_AS uint8_t* kt, int nvalid, int tid) {
+  const int n = (kTK - nvalid) * 64;
+  for (int idx = tid; idx < n; idx += 256) {
+    const int kr = nvalid + (idx >> 6);
+    const int c = idx & 63;
+    *reinterpret_cast<LDS_AS u32x4*>(kt + tile_off(kr, c)) = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
 template <int RB>
-__global__ __launch_bounds__(kDecodeThreads, 1) void decode_dense_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) {
   constexpr int MB = 16 * RB;
-  constexpr bool kAllQK = RB == 4;  // every wave owns a 16-row block of scores
   __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[kDLdsBytes];
   LDS_AS uint8_t* smem = (LDS_AS uint8_t*)(smem_raw);  // C-style: generic -> LDS address space
   LDS_AS float* alpha_s = reinterpret_cast<LDS_AS float*>(smem + kDOffAlpha);  // [2][64]
-  LDS_AS int* flag_s = reinterpret_cast<LDS_AS int*>(smem + kDOffFlag);        // [2][4]
+  LDS_AS uint8_t* flag_s = smem + kDOffFlag;  // [2][4] bytes: one 32-bit word per tile parity
   LDS_AS float* l_s = reinterpret_cast<LDS_AS float*>(smem + kDOffL);
+  LDS_AS int* pages_s = reinterpret_cast<LDS_AS int*>(smem + kDOffPages);
 
   const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool is_qk = wv < 4;
+  const int w = wv & 3;
   const int l = tid & 63, g = l >> 4, li = l & 15;
-  const bool qk_wave = kAllQK || w < RB;
+  const bool has_rows = is_qk && w < RB;
   const int part = blockIdx.x, rbk = blockIdx.y;
   const int begin_req = ld_const(a.sched_meta, part * 8 + 0);
   if (begin_req < 0) return;
@@ -710,14 +806,23 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_dense_kernel(DecodeA
   }
 
   TileLoader<false> loader;
-  loader.init(w, l);
+  loader.init(w, l);  // used by the PV waves only (same split of a tile as 4 waves)
   const int kx = li & 7;
   const uint32_t kq_base0 = (uint32_t)(li * kRowBytes + 16 * (4 * (0 ^ (kx >> 2)) + (g ^ (kx & 3))));
   const uint32_t kq_base1 = (uint32_t)(li * kRowBytes + 16 * (4 * (1 ^ (kx >> 2)) + (g ^ (kx & 3))));
-  const int kr0 = 8 * g + (li >> 2);        // transposed V read: key row of this lane (and +4)
+  // Transposed V reads: lane group g needs keys 8g..8g+7 of the tile, read as two
+  // 4-key halves.  Odd groups read the upper half first, so that in each read
+  // the 16 rows cover every residue mod 8 twice and the chunk swizzle spreads
+  // them over all banks (in natural order two of the four groups collide).  The
+  // key order inside the MFMA contraction changes accordingly, and the QK waves
+  // store P with the two halves of odd 8-key blocks swapped to match.
+  const int kr0 = 8 * g + (li >> 2) + 4 * (g & 1);
+  const int kr1 = 8 * g + (li >> 2) + 4 * ((g & 1) ^ 1);
+  const int p_off = 8 * (g ^ (g >> 1));  // byte offset of this lane's 4 keys in a P row
   const int tr_j = li & 3;
   const uint32_t tr_within = (tr_j & 1) * 8;
   const int row_local = 16 * w + li;
+  MLA_PROF_DECL
 
   for (int r = begin_req; r <= end_req; ++r) {
     int seqlen = ld_const(a.seqlens, r);
@@ -739,187 +844,274 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_dense_kernel(DecodeA
       if (threadIdx.x == 0) atomicOr(&g_error_flags, kErrMeta);
       continue;
     }
-
     const int rho = rbk * MB + row_local;
-    const bool live = qk_wave && rho < a.M;
-    bf16x8 qreg[18];
-    {
-      const uint16_t* qrow = a.q + ((int64_t)r * a.M + (live ? rho : 0)) * kDQK + 8 * g;
-#pragma unroll
-      for (int s = 0; s < 18; ++s) {
-        const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 32 * s);
-        qreg[s] = live ? v : bf16x8{};
-      }
-    }
-    int lim = 0;
-    if (live) {
-      int nvis = seqlen;
-      if (a.causal) nvis = min(max(seqlen - a.s_q + rho / a.h_q + 1, 0), seqlen);
-      lim = min(t1, nvis);
-    }
-    float mrow = -INFINITY, lpart = 0.f;
-    f32x4 o[8][RB];
-#pragma unroll
-    for (int db = 0; db < 8; ++db)
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-    for (int tt = 0; tt < kStages - 1; ++tt)
-      if (tt < ntile) loader.issue(a, r, t0 + tt * kTK, smem, tt, w);
-
-    // softmax of tile t: scores in acc -> P (bf16) into P buffer t&1, rescale factor and flag
-    auto softmax = [&](int t, const f32x4 (&acc)[2]) {
-      const int key0 = t0 + t * kTK;
-      float sv[8];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = acc[kb][i] * a.scale_log2;
-          sv[kb * 4 + i] = key0 + 16 * kb + 4 * g + i < lim ? x : -INFINITY;
-          mx = fmaxf(mx, sv[kb * 4 + i]);
-        }
-      mx = row4_max(mx);
-      const float mold = mrow;
-      const bool upd = mx > mold + kRescaleThreshold;
-      const float mnew = upd ? mx : mold;
-      const float alpha = upd ? fast_exp2(mold - mnew) : 1.f;
-      mrow = mnew;
-      const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-      float pv[8];
-      float psum = 0.f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        pv[k] = fast_exp2(sv[k] - mref);
-        psum += pv[k];
-      }
-      lpart = lpart * alpha + psum;
-      LDS_AS uint8_t* prow = smem + kDOffP + (t & 1) * kPBufBytes + row_local * kPStride + 8 * g;
-      *reinterpret_cast<LDS_AS u32x2*>(prow) = u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
-      *reinterpret_cast<LDS_AS u32x2*>(prow + 32) = u32x2{pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
-      if (g == 0) alpha_s[(t & 1) * kMaxRowsPerWG + row_local] = alpha;
-      const bool any = __any(upd);
-      if (l == 0) flag_s[(t & 1) * 4 + w] = any ? 1 : 0;
-    };
-
-    // operands of PV(t): P^T rows of every row block, V^T of the wave's 8 column blocks
-    struct PvOps {
-      bf16x8 bp[RB];
-      bf16x4 v[8][2];
-    };
-    auto pv_issue = [&](int t, PvOps& op) {
-      const LDS_AS uint8_t* pb = smem + kDOffP + (t & 1) * kPBufBytes;
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) op.bp[rb] = lds_read_b128(pb + (16 * rb + li) * kPStride + 16 * g);
-      const LDS_AS uint8_t* kt = smem + kOffKDense + (t & 3) * kTileBytes;
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const int c = 16 * w + 2 * db + (tr_j >> 1);
-        op.v[db][0] = lds_read_tr16(kt + tile_off(kr0, c) + tr_within);
-        op.v[db][1] = lds_read_tr16(kt + tile_off(kr0 + 4, c) + tr_within);
-      }
-    };
-    auto pv_finish = [&](int t, PvOps& op) {
-      if (t > 0) {  // O is still zero before the first tile: nothing to rescale
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          if (flag_s[(t & 1) * 4 + rb]) {
-            const float al = alpha_s[(t & 1) * kMaxRowsPerWG + 16 * rb + li];
-#pragma unroll
-            for (int db = 0; db < 8; ++db) o[db][rb] *= al;
-          }
-        }
-      }
-    };
-    auto pv_mfma = [&](PvOps& op) {
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const bf16x8 av = __builtin_shufflevector(op.v[db][0], op.v[db][1], 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) o[db][rb] = mfma16(av, op.bp[rb], o[db][rb]);
-      }
-    };
-    // end of iteration t: tile t+1 resident and visible, P(t) visible, ring slot of t-1 refilled
-    auto advance = [&](int t) {
-      if (t + 1 < ntile) {
-        if (t + 2 < ntile) wait_vmcnt<kLPW>();
-        else wait_vmcnt<0>();
-      }
-      sync_lds();
-      if (t + 3 < ntile) loader.issue(a, r, t0 + (t + 3) * kTK, smem, (t + 3) & 3, w);
-    };
-    auto tail_fixup = [&](int t) {
-      const int nvalid = min(kTK, t1 - (t0 + t * kTK));
-      if (nvalid < kTK) zero_tail_rows(smem + kOffKDense + (t & 3) * kTileBytes, nvalid);
-    };
-
-    if (ntile > 0) {
-      if (ntile > 2) wait_vmcnt<2 * kLPW>();
-      else if (ntile > 1) wait_vmcnt<kLPW>();
-      else wait_vmcnt<0>();
-      sync_lds();
-      // iteration 0: QK^T and softmax only
-      tail_fixup(0);
-      if (qk_wave) {
-        f32x4 acc[2];
-        qk_tile(smem + kOffKDense, kq_base0, kq_base1, qreg, acc);
-        softmax(0, acc);
-      }
-      advance(0);
-      for (int t = 1; t < ntile; ++t) {
-        tail_fixup(t);
-        PvOps op;
-        pv_issue(t - 1, op);
-        f32x4 acc[2];
-        if (qk_wave) qk_tile(smem + kOffKDense + (t & 3) * kTileBytes, kq_base0, kq_base1, qreg, acc);
-        pv_finish(t - 1, op);
-        pv_mfma(op);
-        if (qk_wave) softmax(t, acc);
-        advance(t);
-      }
-      PvOps op;
-      pv_issue(ntile - 1, op);
-      pv_finish(ntile - 1, op);
-      pv_mfma(op);
-    }
-
-    // ---- epilogue: row sums to LDS, then normalise and store
-    if (qk_wave) {
-      const float lt = row4_sum(lpart);
-      if (g == 0) {
-        l_s[row_local] = lt;
-        if (rho < a.M) {
-          const float lse = lt > 0.f ? (mrow + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
-          if (nsplit == 1) a.lse[(int64_t)r * a.M + rho] = lse;
-          else a.part_lse[(int64_t)slot * a.M + rho] = lse;
-        }
-      }
-    }
+    // page ids of this piece's first kPageCache blocks -> LDS (the tile loop then
+    // never waits on a scalar load); later blocks, if any, are looked up directly
+    const int ncache = min(blk1 - blk0, kPageCache);
+    for (int i = tid; i < ncache; i += kWsThreads)
+      pages_s[i] = a.block_table[(int64_t)r * a.max_pages + blk0 + i];
     sync_lds();
+    // page id of tile t: an LDS read (or, past the cached range, a scalar load)
+    // that is made wave-uniform only where it is used
+    auto page_raw = [&](int t) -> int {
+      const int b = (t0 + t * kTK) / kPage - blk0;
+      return b < kPageCache ? pages_s[b] : ld_const(a.block_table, (int64_t)r * a.max_pages + blk0 + b);
+    };
+    auto uniform = [](int raw) -> int64_t { return __builtin_amdgcn_readfirstlane(raw); };
+
+    if (is_qk) {
+      // ================================================================ QK waves
+      const bool live = has_rows && rho < a.M;
+      bf16x8 qreg[18];
+      {
+        const uint16_t* qrow = a.q + ((int64_t)r * a.M + (live ? rho : 0)) * kDQK + 8 * g;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int rho_o = rbk * MB + 16 * rb + li;
-      if (rho_o >= a.M) continue;
-      const float lt = l_s[16 * rb + li];
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      if (nsplit == 1) {
-        uint16_t* orow = a.out + ((int64_t)r * a.M + rho_o) * kDV + 128 * w + 4 * g;
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          const f32x4 v = o[db][rb] * inv;
-          *reinterpret_cast<u32x2*>(orow + 16 * db) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        for (int s = 0; s < 18; ++s) {
+          const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 32 * s);
+          qreg[s] = live ? v : bf16x8{};
         }
-      } else {
-        float* prow = a.part_o + ((int64_t)slot * a.M + rho_o) * kDV + 128 * w + 4 * g;
-#pragma unroll
-        for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(prow + 16 * db) = o[db][rb] * inv;
       }
+      int lim = 0;
+      if (live) {
+        int nvis = seqlen;
+        if (a.causal) nvis = min(max(seqlen - a.s_q + rho / a.h_q + 1, 0), seqlen);
+        lim = min(t1, nvis);
+      }
+      float mrow = -INFINITY, lpart = 0.f;
+      f32x4 sacc[2];  // raw scores of the tile whose softmax runs in the next iteration
+
+      // Online softmax of tile ts from its raw scores `sc`, in steps so that the
+      // caller can spread it over the MFMAs of the next tile: step 0 scales,
+      // masks and reduces the row max; 1 decides the rescale; 2 exponentiates and
+      // sums; 3 writes P, the factor and the flag.
+      float sv[8], pv[8], mx = -INFINITY, alpha = 1.f;
+      bool upd = false;
+      auto softmax_step = [&](int step, int ts, const f32x4 (&sc)[2]) {
+        if (step == 0) {
+          const int key0 = t0 + ts * kTK;
+          // keys past a row's visible range score -inf; when every row of the
+          // wave sees the whole tile the masking is skipped
+          const bool whole = __all(!live || key0 + kTK <= lim);
+          mx = -INFINITY;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float x = sc[kb][i] * a.scale_log2;
+              sv[kb * 4 + i] = (whole || key0 + 16 * kb + 4 * g + i < lim) ? x : -INFINITY;
+              mx = fmaxf(mx, sv[kb * 4 + i]);
+            }
+          mx = row4_max(mx);
+        } else if (step == 1) {
+          const float mold = mrow;
+          upd = mx > mold + kRescaleThreshold;
+          const float mnew = upd ? mx : mold;
+          alpha = upd ? fast_exp2(mold - mnew) : 1.f;
+          mrow = mnew;
+        } else if (step == 2) {
+          const float mref = (mrow == -INFINITY) ? 0.f : mrow;
+          float psum = 0.f;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            pv[k] = fast_exp2(sv[k] - mref);
+            psum += pv[k];
+          }
+          lpart = lpart * alpha + psum;
+        } else {
+          LDS_AS uint8_t* prow = smem + kDOffP + (ts & 1) * kPBufBytes + row_local * kPStride + p_off;
+          *reinterpret_cast<LDS_AS u32x2*>(prow) = u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
+          *reinterpret_cast<LDS_AS u32x2*>(prow + 32) = u32x2{pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
+          if (g == 0) alpha_s[(ts & 1) * kMaxRowsPerWG + row_local] = alpha;
+          const bool any = __any(upd);
+          if (l == 0) flag_s[(ts & 1) * 4 + w] = any ? 1 : 0;
+        }
+      };
+
+      if (ntile > 0) sync_lds();  // tile 0 resident
+      MLA_PROF_RESET
+      // one iteration; DO_QK: S(t) = QK^T(t), DO_SM: softmax of S(t-1) (in the
+      // shadow of the MFMAs when both run).  Instantiated per stage combination.
+      auto iter = [&](auto do_qk_c, auto do_sm_c, int t) {
+        constexpr bool DO_QK = decltype(do_qk_c)::value;
+        constexpr bool DO_SM = decltype(do_sm_c)::value;
+        if (has_rows) {
+          if constexpr (DO_QK) {
+            f32x4 acc[2];
+            const LDS_AS uint8_t* kt = smem + kOffKDense + (t & 3) * kTileBytes;
+            if constexpr (DO_SM) {
+              const f32x4 prev[2] = {sacc[0], sacc[1]};
+              // one softmax step after each of the first four k-steps
+              qk_tile<kQkDepth>(kt, kq_base0, kq_base1, qreg, acc, [&](int s) {
+                if (s < 4) softmax_step(s, t - 1, prev);
+              });
+            } else {
+              qk_tile<kQkDepth>(kt, kq_base0, kq_base1, qreg, acc);
+            }
+            sacc[0] = acc[0];
+            sacc[1] = acc[1];
+          } else if constexpr (DO_SM) {
+#pragma unroll
+            for (int step = 0; step < 4; ++step) softmax_step(step, t - 1, sacc);
+          }
+          if (t == ntile) {  // every tile's softmax is done: row sums for the output stage
+            const float lt = row4_sum(lpart);
+            if (g == 0) {
+              l_s[row_local] = lt;
+              if (rho < a.M) {
+                const float lse = lt > 0.f ? (mrow + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
+                if (nsplit == 1) a.lse[(int64_t)r * a.M + rho] = lse;
+                else a.part_lse[(int64_t)slot * a.M + rho] = lse;
+              }
+            }
+          }
+          MLA_PROF(0);
+        }
+        sync_lds();
+        MLA_PROF(2);
+      };
+      using F = std::false_type;
+      using T = std::true_type;
+      // t = 0: QK only; 1..ntile-1: QK + softmax(t-1); ntile: softmax only;
+      // ntile+1: nothing (the PV waves drain)
+      if (ntile >= 1) {
+        iter(T{}, F{}, 0);
+        for (int t = 1; t < ntile; ++t) iter(T{}, T{}, t);
+        iter(F{}, T{}, ntile);
+      } else {
+        iter(F{}, F{}, 0);
+      }
+      iter(F{}, F{}, ntile + 1);
+      MLA_PROF_TILES(ntile)
+    } else {
+      // ================================================================ PV waves
+      f32x4 o[8][RB];
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      bf16x4 v[8][2];  // V^T fragments of one tile (this wave's 128 columns, 32 keys)
+      auto vread = [&](int t, int db) {
+        const LDS_AS uint8_t* kt = smem + kOffKDense + (t & 3) * kTileBytes;
+        const int c = 16 * w + 2 * db + (tr_j >> 1);
+        v[db][0] = lds_read_tr16(kt + tile_off(kr0, c) + tr_within);
+        v[db][1] = lds_read_tr16(kt + tile_off(kr1, c) + tr_within);
+      };
+
+      // tiles 0 and 1 now; tile t+2 during iteration t
+      if (ntile > 0) loader.issue_page(a, uniform(page_raw(0)), t0, smem, 0, w);
+      if (ntile > 1) loader.issue_page(a, uniform(page_raw(1)), t0 + kTK, smem, 1, w);
+      // page id of the tile the next iteration loads: read before the barrier that
+      // ends an iteration (which waits for it) and made wave-uniform right after
+      // it, when no other LDS read is pending, so that the wait costs nothing
+      int pg_next = ntile > 2 ? page_raw(2) : 0;
+      if (ntile > 1) wait_vmcnt<kLPW>();
+      else wait_vmcnt<0>();
+      if (ntile > 0) sync_lds();  // tile 0 resident
+      MLA_PROF_RESET
+      // one iteration; DO_PV: PV(t-2) from registers, DO_VREAD: V(t-1) into
+      // registers.  Instantiated per stage combination so that the steady-state
+      // loop carries no stage conditions (and no register copies for them).
+      auto iter = [&](auto do_pv_c, auto do_vread_c, int t) {
+        constexpr bool DO_PV = decltype(do_pv_c)::value;
+        constexpr bool DO_VREAD = decltype(do_vread_c)::value;
+        const int64_t pg = uniform(pg_next);
+        if (t < ntile) {
+          const int nvalid = min(kTK, t1 - (t0 + t * kTK));
+          if (nvalid < kTK) zero_tail_rows_256(smem + kOffKDense + (t & 3) * kTileBytes, nvalid, tid - 256);
+        }
+        const int tp = t - 2, tv = t - 1;
+        // PV(t-2) operands from LDS first: rescale flags and factors, P^T
+        uint32_t fl = 0;
+        float al[RB];
+        bf16x8 bp[RB];
+        if constexpr (DO_PV) {
+          const LDS_AS uint8_t* pb = smem + kDOffP + (tp & 1) * kPBufBytes;
+          fl = *reinterpret_cast<const LDS_AS uint32_t*>(flag_s + (tp & 1) * 4);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) al[rb] = alpha_s[(tp & 1) * kMaxRowsPerWG + 16 * rb + li];
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) bp[rb] = lds_read_b128(pb + (16 * rb + li) * kPStride + 16 * g);
+        }
+        // loads of tile t+2 into the slot of tile t-2
+        const bool more = t + 2 < ntile;
+        if (more) {
+          const uint8_t* nsrc = loader.tile_src(a, pg, t0 + (t + 2) * kTK);
+#pragma unroll
+          for (int k = 0; k < kLPW; ++k) loader.issue_one(nsrc, smem, (t + 2) & 3, w, k);
+        }
+        MLA_PROF(6);
+        if constexpr (DO_PV) {
+          if (tp > 0) {  // O is still zero before the first tile: nothing to rescale
+            const uint32_t fls = __builtin_amdgcn_readfirstlane(fl);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+              if ((fls >> (8 * rb)) & 0xffu) {
+#pragma unroll
+                for (int db = 0; db < 8; ++db) o[db][rb] *= al[rb];
+              }
+            }
+          }
+#pragma unroll
+          for (int db = 0; db < 8; ++db) {
+            const bf16x8 av = __builtin_shufflevector(v[db][0], v[db][1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) o[db][rb] = mfma16(av, bp[rb], o[db][rb]);
+            if constexpr (DO_VREAD) vread(tv, db);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else if constexpr (DO_VREAD) {
+#pragma unroll
+          for (int db = 0; db < 8; ++db) vread(tv, db);
+        }
+        MLA_PROF(3);
+        // own loads of tile t+1 done (tile t+2 may stay in flight)
+        if (t + 1 < ntile) {
+          if (more) wait_vmcnt<kLPW>();
+          else wait_vmcnt<0>();
+        }
+        MLA_PROF(4);
+        if (t + 3 < ntile) pg_next = page_raw(t + 3);
+        sync_lds();
+        MLA_PROF(5);
+      };
+      using F = std::false_type;
+      using T = std::true_type;
+      iter(F{}, F{}, 0);
+      if (ntile >= 1) {
+        iter(F{}, T{}, 1);
+        for (int t = 2; t <= ntile; ++t) iter(T{}, T{}, t);
+        iter(T{}, F{}, ntile + 1);
+      } else {
+        iter(F{}, F{}, 1);
+      }
+      MLA_PROF_TILES(ntile)
+      sync_lds();  // l from the QK waves (written in iteration ntile)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int rho_o = rbk * MB + 16 * rb + li;
+        if (rho_o >= a.M) continue;
+        const float lt = l_s[16 * rb + li];
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        if (nsplit == 1) {
+          uint16_t* orow = a.out + ((int64_t)r * a.M + rho_o) * kDV + 128 * w + 4 * g;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) {
+            const f32x4 vv = o[db][rb] * inv;
+            *reinterpret_cast<u32x2*>(orow + 16 * db) = u32x2{pack_bf16x2(vv[0], vv[1]), pack_bf16x2(vv[2], vv[3])};
+          }
+        } else {
+          float* prow = a.part_o + ((int64_t)slot * a.M + rho_o) * kDV + 128 * w + 4 * g;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(prow + 16 * db) = o[db][rb] * inv;
+        }
+      }
+      wait_vmcnt<0>();  // the next request's loads must not overtake this one's stores in the count
     }
-    wait_vmcnt<0>();
+    if (is_qk) sync_lds();  // matches the PV waves' extra barrier before the output stage
+    // every LDS buffer is reused by the next request of this partition
     sync_lds();
   }
+  MLA_PROF_DUMP((blockIdx.y * gridDim.x + blockIdx.x) * 8 + wv)
 }
 
 // 16-row blocks per workgroup.  Capped at 4 (64 rows): at 128 rows the Q and O
@@ -940,7 +1132,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   if constexpr (FP8)
     hipLaunchKernelGGL((decode_kernel<RB, true>), grid, dim3(kDecodeThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_dense_kernel<RB>), grid, dim3(kDecodeThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_ws_kernel<RB>), grid, dim3(kWsThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -957,13 +1149,13 @@ hipError_t decode_occupancy(bool fp8, int M, int* wgs_per_cu) {
   hipError_t e;
   switch (decode_row_blocks_per_wg(M)) {
     case 1: e = fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<1, true>, kDecodeThreads, 0)
-                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_dense_kernel<1>, kDecodeThreads, 0);
+                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_ws_kernel<1>, kWsThreads, 0);
       break;
     case 2: e = fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<2, true>, kDecodeThreads, 0)
-                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_dense_kernel<2>, kDecodeThreads, 0);
+                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_ws_kernel<2>, kWsThreads, 0);
       break;
     default: e = fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<4, true>, kDecodeThreads, 0)
-                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_dense_kernel<4>, kDecodeThreads, 0);
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_ws_kernel<4>, kWsThreads, 0);
       break;
   }
   *wgs_per_cu = n;
