@@ -141,7 +141,8 @@ int mla_get_decode_metadata(const int32_t* seqlens, int batch, int s_q, int h_q,
  *                (then block_table/max_pages/num_pages are ignored, seqlens is
  *                topk_length, s_q must be 1, h_q must be 64 or 128, no causal)
  *   block_table (device) int32 [batch][max_pages], seqlens (device) int32 [batch]
- *   softmax_scale: multiplies q.k (e.g. 576^-0.5); causal: 0/1
+ *   softmax_scale: multiplies q.k (e.g. 576^-0.5); must be finite and > 0, else
+ *                  MLA_ERR_INVALID_ARGUMENT; causal: 0/1
  *   sched_meta, num_splits (device): from mla_get_decode_metadata with the same
  *     seqlens, batch and num_parts
  *   out (device) bf16 [batch][s_q][h_q][512], lse (device) fp32 [batch][s_q][h_q]

@@ -4,6 +4,7 @@
 // packed path's "Supported scope" on FlashMLA PR 200 asks of unsupported
 // shapes), the occupancy-derived split count (FlashMLA PR 183, "How the
 // occupancy work went"), workspace sizing and kernel dispatch.
+#include <cmath>
 #include "../../include/mla_paged_kv.h"
 
 #include <stdarg.h>
@@ -173,7 +174,8 @@ int mla_decode_fwd(const void* q, const void* kv, int kv_format, int64_t num_pag
   }
   if (num_parts < 1 || num_parts > MLA_MAX_PARTS)
     return fail(MLA_ERR_INVALID_ARGUMENT, "num_parts %d out of [1, %d]", num_parts, MLA_MAX_PARTS);
-  if (!(softmax_scale == softmax_scale)) return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale is NaN");
+  if (!(softmax_scale > 0.f) || !(softmax_scale < INFINITY))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0 (got %g)", (double)softmax_scale);
   const size_t need = mla_decode_workspace_size(batch, s_q, h_q, num_parts);
   if (!workspace || workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "decode workspace %zu B < %zu B", workspace_bytes, need);

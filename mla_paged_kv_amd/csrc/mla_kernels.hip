@@ -133,16 +133,19 @@ __device__ __forceinline__ void load_lds16(const void* gsrc, LDS_AS void* ldst) 
 
 // Same, with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane offset
 // (saddr form): no per-lane 64-bit address arithmetic.
-__device__ __forceinline__ void load_lds16_s(const void* sbase, uint32_t voff, LDS_AS void* ldst) {
+// `bu` must be wave-uniform and already in SGPRs (see uniform_u64).
+__device__ __forceinline__ void load_lds16_s(uint64_t bu, uint32_t voff, LDS_AS void* ldst) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)ldst);
-  // the base is wave-uniform by contract; readfirstlane makes that visible so
-  // that it is allocated to SGPRs.  The builtin returns a signed int: each half
-  // goes through uint32_t so that the low word is zero-extended, not sign-extended.
-  const uint64_t b = (uint64_t)(uintptr_t)sbase;
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(bu), "s"(m0v) : "memory");
+}
+
+// A wave-uniform 64-bit value made visible as such (SGPRs).  The builtin returns
+// a signed int: each half goes through uint32_t so that the low word is
+// zero-extended, not sign-extended.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t b) {
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-  const uint64_t bu = ((uint64_t)hi << 32) | (uint64_t)lo;
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(bu), "s"(m0v) : "memory");
+  return ((uint64_t)hi << 32) | (uint64_t)lo;
 }
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const LDS_AS uint8_t* p) {
@@ -178,6 +181,18 @@ __device__ __forceinline__ void permlane_pair16(float& a, float& b) {
 }
 __device__ __forceinline__ void permlane_pair32(float& a, float& b) {
   asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+// One step of the row max: max(v[l], v[l ^ 16]) (resp. l ^ 32) in one asm block,
+// so that the compiler adds no NaN-quieting ops around the permlane results.
+__device__ __forceinline__ float rowmax16(float v) {
+  float b = v;
+  asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\tv_max_f32 %0, %0, %1" : "+v"(v), "+v"(b));
+  return v;
+}
+__device__ __forceinline__ float rowmax32(float v) {
+  float b = v;
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\tv_max_f32 %0, %0, %1" : "+v"(v), "+v"(b));
+  return v;
 }
 __device__ __forceinline__ float row4_max(float v) {
   float a = v, b = v;
@@ -334,23 +349,25 @@ struct TileLoader<false> {
   }
   // Same, with the page id already looked up (wave-uniform).
   __device__ void issue_page(const DecodeArgs& a, int64_t page, int key0, LDS_AS uint8_t* smem, int st, int w) {
-    const uint8_t* src = tile_src(a, page, key0);
+    const uint64_t src = tile_src(a, page, key0);
 #pragma unroll
     for (int k = 0; k < kLoadsPerWave; ++k) issue_one(src, smem, st, w, k);
   }
-  // Base addresses of tile (page, key0) for issue_one.
-  __device__ const uint8_t* tile_src(const DecodeArgs& a, int64_t page, int key0) const {
+  // Wave-uniform base address of tile (page, key0) for issue_one, in SGPRs.
+  __device__ uint64_t tile_src(const DecodeArgs& a, int64_t page, int key0) const {
     if (page < 0 || page >= a.num_pages) {
       if ((threadIdx.x & 63) == 0) atomicOr(&g_error_flags, kErrPage);
       page = 0;  // stay in bounds; the output of this request is undefined
     }
-    return a.kv + page * (int64_t)(kPage * kRowBytes) + (key0 & 63) * kRowBytes;
+    // 32 x 32 -> 64-bit product: page < 2^31
+    const uint64_t off = (uint64_t)(uint32_t)page * (uint32_t)(kPage * kRowBytes) + (uint32_t)((key0 & 63) * kRowBytes);
+    return uniform_u64((uint64_t)(uintptr_t)a.kv + off);
   }
   // The k-th of this wave's kLoadsPerWave loads of a tile.
-  __device__ void issue_one(const uint8_t* src, LDS_AS uint8_t* smem, int st, int w, int k) const {
+  __device__ void issue_one(uint64_t src, LDS_AS uint8_t* smem, int st, int w, int k) const {
     const int qi = w + 4 * k;
     const uint32_t voff = l56 + 16u * ((bits >> (3 * k)) & 7u);
-    load_lds16_s(src + qi * 1024, voff, smem + kOffKDense + st * kTileBytes + qi * 1024);
+    load_lds16_s(src + (uint64_t)(qi * 1024), voff, smem + kOffKDense + st * kTileBytes + qi * 1024);
   }
 };
 
@@ -732,18 +749,23 @@ __device__ __forceinline__ void qk_tile(const LDS_AS uint8_t* kt, uint32_t base0
     k0[s] = lds_read_b128(kt + addr(s));
     k1[s] = lds_read_b128(kt + addr(s) + 16 * kRowBytes);
   }
-  acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // four independent accumulation chains (key block x k-step parity): an MFMA
+  // then waits for the one issued two k-steps earlier, not one
+  f32x4 c[2][2];
+  c[0][0] = c[0][1] = c[1][0] = c[1][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < 18; ++s) {
     if (s + D - 1 < 18) {
       k0[(s + D - 1) % D] = lds_read_b128(kt + addr(s + D - 1));
       k1[(s + D - 1) % D] = lds_read_b128(kt + addr(s + D - 1) + 16 * kRowBytes);
     }
-    acc[0] = mfma16(k0[s % D], qreg[s], acc[0]);
-    acc[1] = mfma16(k1[s % D], qreg[s], acc[1]);
+    c[0][s & 1] = mfma16(k0[s % D], qreg[s], c[0][s & 1]);
+    c[1][s & 1] = mfma16(k1[s % D], qreg[s], c[1][s & 1]);
     hook(s);
     __builtin_amdgcn_sched_barrier(0);
   }
+  acc[0] = c[0][0] + c[0][1];
+  acc[1] = c[1][0] + c[1][1];
 }
 
 // ------------------------------------------------------------------ dense decode, wave-specialised
@@ -789,8 +811,9 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
 
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Waves w and w+4 share a SIMD: each SIMD runs one QK and one PV wave.
   const bool is_qk = wv < 4;
-  const int w = wv & 3;
+  const int w = wv & 3;  // index within the role
   const int l = tid & 63, g = l >> 4, li = l & 15;
   const bool has_rows = is_qk && w < RB;
   const int part = blockIdx.x, rbk = blockIdx.y;
@@ -880,50 +903,95 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
       float mrow = -INFINITY, lpart = 0.f;
       f32x4 sacc[2];  // raw scores of the tile whose softmax runs in the next iteration
 
-      // Online softmax of tile ts from its raw scores `sc`, in steps so that the
-      // caller can spread it over the MFMAs of the next tile: step 0 scales,
-      // masks and reduces the row max; 1 decides the rescale; 2 exponentiates and
-      // sums; 3 writes P, the factor and the flag.
-      float sv[8], pv[8], mx = -INFINITY, alpha = 1.f;
+      // Online softmax of tile ts from its raw scores `sc`, in 18 steps, one per
+      // k-step of the next tile's QK^T: the waves issue in order, so a dependent
+      // VALU op stalls the MFMAs behind it; one dependency level per k-step lets
+      // the two MFMAs of that step cover its latency.  The scale c > 0 (checked at
+      // the boundary) is applied as max(c s) = c max(s) and exp2(c s - m) =
+      // exp2(fma(s, c, -m)), one op per score.
+      float x[8], pv[8], mx = 0.f, ma = 0.f, mb = 0.f, alpha = 1.f, nmref = 0.f, s01 = 0.f, s23 = 0.f,
+            s45 = 0.f, s67 = 0.f, pw = 0.f;
+      uint32_t wp[4] = {0u, 0u, 0u, 0u};
       bool upd = false;
       auto softmax_step = [&](int step, int ts, const f32x4 (&sc)[2]) {
-        if (step == 0) {
-          const int key0 = t0 + ts * kTK;
-          // keys past a row's visible range score -inf; when every row of the
-          // wave sees the whole tile the masking is skipped
-          const bool whole = __all(!live || key0 + kTK <= lim);
-          mx = -INFINITY;
+        switch (step) {
+          case 0:
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+            for (int i = 0; i < 4; ++i) x[i] = sc[0][i];
+            break;
+          case 1:
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float x = sc[kb][i] * a.scale_log2;
-              sv[kb * 4 + i] = (whole || key0 + 16 * kb + 4 * g + i < lim) ? x : -INFINITY;
-              mx = fmaxf(mx, sv[kb * 4 + i]);
+            for (int i = 0; i < 4; ++i) x[4 + i] = sc[1][i];
+            break;
+          case 2: {
+            // keys past a row's visible range score -inf; skipped when every row
+            // of the wave sees the whole tile
+            const int key0 = t0 + ts * kTK;
+            if (!__all(!live || key0 + kTK <= lim)) {
+#pragma unroll
+              for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  if (key0 + 16 * kb + 4 * g + i >= lim) x[kb * 4 + i] = -INFINITY;
             }
-          mx = row4_max(mx);
-        } else if (step == 1) {
-          const float mold = mrow;
-          upd = mx > mold + kRescaleThreshold;
-          const float mnew = upd ? mx : mold;
-          alpha = upd ? fast_exp2(mold - mnew) : 1.f;
-          mrow = mnew;
-        } else if (step == 2) {
-          const float mref = (mrow == -INFINITY) ? 0.f : mrow;
-          float psum = 0.f;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            pv[k] = fast_exp2(sv[k] - mref);
-            psum += pv[k];
+            break;
           }
-          lpart = lpart * alpha + psum;
-        } else {
-          LDS_AS uint8_t* prow = smem + kDOffP + (ts & 1) * kPBufBytes + row_local * kPStride + p_off;
-          *reinterpret_cast<LDS_AS u32x2*>(prow) = u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
-          *reinterpret_cast<LDS_AS u32x2*>(prow + 32) = u32x2{pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
-          if (g == 0) alpha_s[(ts & 1) * kMaxRowsPerWG + row_local] = alpha;
-          const bool any = __any(upd);
-          if (l == 0) flag_s[(ts & 1) * 4 + w] = any ? 1 : 0;
+          case 3:
+            ma = fmaxf(fmaxf(x[0], x[1]), x[2]);
+            mb = fmaxf(fmaxf(x[3], x[4]), x[5]);
+            break;
+          case 4: ma = fmaxf(fmaxf(x[6], x[7]), ma); break;
+          case 5: mx = fmaxf(ma, mb); break;
+          case 6: mx = rowmax16(mx); break;
+          case 7: mx = rowmax32(mx); break;
+          case 8: mx *= a.scale_log2; break;
+          case 9: upd = mx > mrow + kRescaleThreshold; break;
+          case 10: {
+            const float mnew = upd ? mx : mrow;
+            pw = mrow - mnew;
+            mrow = mnew;
+            break;
+          }
+          case 11:
+            alpha = upd ? fast_exp2(pw) : 1.f;  // 0 when the old max was -inf
+            nmref = (mrow == -INFINITY) ? 0.f : -mrow;
+            break;
+          case 12:
+#pragma unroll
+            for (int k = 0; k < 4; ++k) pv[k] = fast_exp2(__builtin_fmaf(x[k], a.scale_log2, nmref));
+            break;
+          case 13:
+#pragma unroll
+            for (int k = 4; k < 8; ++k) pv[k] = fast_exp2(__builtin_fmaf(x[k], a.scale_log2, nmref));
+            break;
+          case 14:
+            s01 = pv[0] + pv[1];
+            s23 = pv[2] + pv[3];
+            s45 = pv[4] + pv[5];
+            s67 = pv[6] + pv[7];
+            break;
+          case 15:
+            wp[0] = pack_bf16x2(pv[0], pv[1]);
+            wp[1] = pack_bf16x2(pv[2], pv[3]);
+            wp[2] = pack_bf16x2(pv[4], pv[5]);
+            wp[3] = pack_bf16x2(pv[6], pv[7]);
+            s01 += s23;
+            s45 += s67;
+            break;
+          case 16: {
+            lpart = lpart * alpha + (s01 + s45);
+            LDS_AS uint8_t* prow = smem + kDOffP + (ts & 1) * kPBufBytes + row_local * kPStride + p_off;
+            *reinterpret_cast<LDS_AS u32x2*>(prow) = u32x2{wp[0], wp[1]};
+            *reinterpret_cast<LDS_AS u32x2*>(prow + 32) = u32x2{wp[2], wp[3]};
+            break;
+          }
+          default: {
+            // the factor is read only for row blocks whose flag is set
+            const bool any = __any(upd);
+            if (any && g == 0) alpha_s[(ts & 1) * kMaxRowsPerWG + row_local] = alpha;
+            if (l == 0) flag_s[(ts & 1) * 4 + w] = any ? 1 : 0;
+            break;
+          }
         }
       };
 
@@ -940,9 +1008,9 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
             const LDS_AS uint8_t* kt = smem + kOffKDense + (t & 3) * kTileBytes;
             if constexpr (DO_SM) {
               const f32x4 prev[2] = {sacc[0], sacc[1]};
-              // one softmax step after each of the first four k-steps
+              // one softmax step after each k-step
               qk_tile<kQkDepth>(kt, kq_base0, kq_base1, qreg, acc, [&](int s) {
-                if (s < 4) softmax_step(s, t - 1, prev);
+                softmax_step(s, t - 1, prev);
               });
             } else {
               qk_tile<kQkDepth>(kt, kq_base0, kq_base1, qreg, acc);
@@ -951,7 +1019,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
             sacc[1] = acc[1];
           } else if constexpr (DO_SM) {
 #pragma unroll
-            for (int step = 0; step < 4; ++step) softmax_step(step, t - 1, sacc);
+            for (int step = 0; step < 18; ++step) softmax_step(step, t - 1, sacc);
           }
           if (t == ntile) {  // every tile's softmax is done: row sums for the output stage
             const float lt = row4_sum(lpart);
@@ -1017,7 +1085,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
         const int64_t pg = uniform(pg_next);
         if (t < ntile) {
           const int nvalid = min(kTK, t1 - (t0 + t * kTK));
-          if (nvalid < kTK) zero_tail_rows_256(smem + kOffKDense + (t & 3) * kTileBytes, nvalid, tid - 256);
+          if (nvalid < kTK) zero_tail_rows_256(smem + kOffKDense + (t & 3) * kTileBytes, nvalid, 64 * w + l);
         }
         const int tp = t - 2, tv = t - 1;
         // PV(t-2) operands from LDS first: rescale flags and factors, P^T
@@ -1035,7 +1103,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
         // loads of tile t+2 into the slot of tile t-2
         const bool more = t + 2 < ntile;
         if (more) {
-          const uint8_t* nsrc = loader.tile_src(a, pg, t0 + (t + 2) * kTK);
+          const uint64_t nsrc = loader.tile_src(a, pg, t0 + (t + 2) * kTK);
 #pragma unroll
           for (int k = 0; k < kLPW; ++k) loader.issue_one(nsrc, smem, (t + 2) & 3, w, k);
         }

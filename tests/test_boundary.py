@@ -97,6 +97,9 @@ def decode_call(**kw):
     (dict(parts=0), ops.MLA_ERR_INVALID_ARGUMENT),
     (dict(parts=100000), ops.MLA_ERR_INVALID_ARGUMENT),
     (dict(scale=float("nan")), ops.MLA_ERR_INVALID_ARGUMENT),
+    (dict(scale=0.0), ops.MLA_ERR_INVALID_ARGUMENT),
+    (dict(scale=-0.04), ops.MLA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("inf")), ops.MLA_ERR_INVALID_ARGUMENT),
     (dict(ws_bytes=100), ops.MLA_ERR_WORKSPACE_TOO_SMALL),
     (dict(ws=NULL), ops.MLA_ERR_WORKSPACE_TOO_SMALL),
 ])
