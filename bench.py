@@ -65,6 +65,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (scales the HBM byte counters)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches instead of HIP-graph replays of the step")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -141,7 +143,7 @@ def main():
         }
         log(f"oracle sample: {dt:.2f}s on {threads} threads; parity ok")
 
-    # ---- warmup, then K timed steps
+    # ---- warmup, then K eager steps with per-kernel events (kernel times, roofline)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -152,6 +154,41 @@ def main():
         step(i, evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
+
+    # ---- the step as a HIP graph (one per pool copy), the way a serving loop
+    # issues it; each graph is checked bitwise against the eager step first,
+    # over several replays with eager work in between
+    launch = "eager"
+    if not args.no_graph:
+        graphs = []
+        for i in range(2):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(2):
+            step(i)
+            torch.cuda.synchronize()
+            ref_o, ref_l = out.clone(), lse.clone()
+            for _ in range(3):
+                out.fill_(0)
+                lse.fill_(0)
+                graphs[i].replay()
+                torch.cuda.synchronize()
+                if not (torch.equal(out, ref_o) and torch.equal(lse, ref_l)):
+                    raise SystemExit(f"graph replay of pool {i} differs from the eager step")
+                step(1 - i)  # eager work between replays
+                torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[i % 2].replay()
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % 2].replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t_start
+        launch = "hip graph per pool copy (metadata, decode, combine)"
 
     meta_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
@@ -191,6 +228,7 @@ def main():
             "batch": b, "s_q": s_q, "h_q": h_q, "seqlen": int(w.seqlens[0]), "page_tokens": 64,
             "num_parts": num_parts, "kv_bytes_per_step": kv_bytes, "flops_per_step": flops,
             "cold_kv": "two pool copies alternate per step",
+            "launch": launch,
         },
         "pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 2),
         "tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 2),

@@ -223,64 +223,98 @@ __device__ __forceinline__ uint32_t tile_off(int kr, int c) {
 // has ceil(len/64) blocks, T in all; with P' = min(P, T), part p < P' owns global
 // blocks [floor(pT/P'), floor((p+1)T/P')) and parts p >= P' own none, so the
 // parts owning one request's blocks are consecutive.
-constexpr int kSchedThreads = 1024;
+constexpr int kSchedThreads = 256;
 
-__device__ __forceinline__ int64_t part_of_block(int64_t g, int64_t T, int64_t P) { return ((g + 1) * P - 1) / T; }
+__device__ __forceinline__ int64_t part_of_block(int64_t g, int64_t T, int64_t P);
+
+// floor(a / b) for 0 <= a < 2^53, 0 < b < 2^31: a double estimate corrected to
+// the exact quotient (64-bit integer division is a long software sequence).
+__device__ __forceinline__ int64_t floordiv_exact(int64_t a, int64_t b) {
+  int64_t q = (int64_t)((double)a / (double)b);
+  while (q * b > a) --q;
+  while ((q + 1) * b <= a) ++q;
+  return q;
+}
+
+__device__ __forceinline__ int64_t part_of_block(int64_t g, int64_t T, int64_t P) {
+  return floordiv_exact((g + 1) * P - 1, T);
+}
+
+// inclusive prefix sum over the 64 lanes of a wave
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// exclusive prefix of `local` over the workgroup's 256 threads; *total = sum
+__device__ __forceinline__ int block_excl_scan(int local, int* total, int32_t* wsum) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(local);
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < kSchedThreads / 64; ++i) base += i < wv ? wsum[i] : 0;
+  int tot = 0;
+#pragma unroll
+  for (int i = 0; i < kSchedThreads / 64; ++i) tot += wsum[i];
+  *total = tot;
+  __syncthreads();  // wsum is reused by the next scan
+  return base + incl - local;
+}
 
 __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const int32_t* __restrict__ lengths, int batch,
                                                               int num_parts, int32_t* __restrict__ meta,
                                                               int32_t* __restrict__ num_splits) {
   __shared__ int32_t cum[kSchedMaxBatch + 1];
-  __shared__ int32_t scan[kSchedThreads];
+  __shared__ int32_t wsum[kSchedThreads / 64];
   const int t = threadIdx.x;
-  const int C = (batch + kSchedThreads - 1) / kSchedThreads;  // <= 8
+  const int C = (batch + kSchedThreads - 1) / kSchedThreads;  // <= 32 consecutive requests per thread
 
   // 1. blocks per request, exclusive prefix -> cum
   int local = 0;
   for (int k = 0; k < C; ++k) {
-    int r = t * C + k;
+    const int r = t * C + k;
     if (r < batch) local += (max(lengths[r], 0) + kPage - 1) / kPage;
   }
-  scan[t] = local;
-  __syncthreads();
-  for (int off = 1; off < kSchedThreads; off <<= 1) {
-    int v = t >= off ? scan[t - off] : 0;
-    __syncthreads();
-    scan[t] += v;
-    __syncthreads();
-  }
-  int run = scan[t] - local;
+  int total = 0;
+  int run = block_excl_scan(local, &total, wsum);
   for (int k = 0; k < C; ++k) {
-    int r = t * C + k;
+    const int r = t * C + k;
     if (r < batch) {
       cum[r] = run;
       run += (max(lengths[r], 0) + kPage - 1) / kPage;
     }
   }
-  if (t == kSchedThreads - 1) cum[batch] = scan[t];
+  if (t == 0) cum[batch] = total;
   __syncthreads();
-  const int64_t T = cum[batch];
+  const int64_t T = total;
   const int64_t P = T < num_parts ? T : num_parts;  // P' (0 when there is no block at all)
 
   // 2. partition records
   for (int p = t; p < num_parts; p += kSchedThreads) {
     int32_t* m = meta + (int64_t)p * 8;
-    const int64_t G0 = p < P ? ((int64_t)p * T) / P : T;
-    const int64_t G1 = p < P ? ((int64_t)(p + 1) * T) / P : T;
+    const int64_t G0 = p < P ? floordiv_exact((int64_t)p * T, P) : T;
+    const int64_t G1 = p < P ? floordiv_exact((int64_t)(p + 1) * T, P) : T;
     if (G1 <= G0) {
       m[0] = m[1] = m[2] = m[3] = m[4] = -1;
     } else {
       // first request whose block range ends after G0 (resp. after G1 - 1)
       int lo = 0, hi = batch - 1;
       while (lo < hi) {
-        int mid = (lo + hi) >> 1;
+        const int mid = (lo + hi) >> 1;
         if (cum[mid + 1] > G0) hi = mid; else lo = mid + 1;
       }
       const int br = lo;
       lo = br;
       hi = batch - 1;
       while (lo < hi) {
-        int mid = (lo + hi) >> 1;
+        const int mid = (lo + hi) >> 1;
         if (cum[mid + 1] >= G1) hi = mid; else lo = mid + 1;
       }
       const int er = lo;
@@ -296,28 +330,20 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const int32_t* __r
   // 3. split counts, exclusive prefix -> num_splits
   int splits_local = 0;
   for (int k = 0; k < C; ++k) {
-    int r = t * C + k;
+    const int r = t * C + k;
     if (r < batch && cum[r + 1] > cum[r])
       splits_local += (int)(part_of_block(cum[r + 1] - 1, T, P) - part_of_block(cum[r], T, P) + 1);
   }
-  __syncthreads();
-  scan[t] = splits_local;
-  __syncthreads();
-  for (int off = 1; off < kSchedThreads; off <<= 1) {
-    int v = t >= off ? scan[t - off] : 0;
-    __syncthreads();
-    scan[t] += v;
-    __syncthreads();
-  }
-  run = scan[t] - splits_local;
+  int stotal = 0;
+  run = block_excl_scan(splits_local, &stotal, wsum);
   for (int k = 0; k < C; ++k) {
-    int r = t * C + k;
+    const int r = t * C + k;
     if (r < batch) {
       num_splits[r] = run;
       if (cum[r + 1] > cum[r]) run += (int)(part_of_block(cum[r + 1] - 1, T, P) - part_of_block(cum[r], T, P) + 1);
     }
   }
-  if (t == kSchedThreads - 1) num_splits[batch] = scan[t];
+  if (t == 0) num_splits[batch] = stotal;
 }
 
 // ------------------------------------------------------------------ decode

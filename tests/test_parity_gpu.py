@@ -244,3 +244,45 @@ def test_out_of_range_page_sets_flag_without_fault():
     flags = ops.mla_read_device_errors()
     assert flags & 1
     assert ops.mla_read_device_errors() == 0
+
+
+# ----------------------------------------------------------------------------- HIP graph capture
+
+def test_hip_graph_replay_matches_eager():
+    """The step (metadata, decode, combine) captured in a HIP graph: every replay
+    equals the eager step bit for bit, with eager work (including on the
+    workspace) between replays."""
+    G.say("hip graph replay")
+    w = W.dense_workload("graph", 130, 4, 1, 128, [700, 64, 2049, 1], pool_pages=60, num_parts=8)
+    t = G.dev_tensors(w)
+    b, s_q, h_q, parts = w.batch, w.s_q, w.h_q, 8
+    dev = torch.device("cuda:0")
+    meta = torch.empty((parts, 8), dtype=torch.int32, device=dev)
+    ns = torch.empty((b + 1,), dtype=torch.int32, device=dev)
+    ws = torch.empty((ops.mla_decode_workspace_size(b, s_q, h_q, parts),), dtype=torch.uint8, device=dev)
+    out = torch.empty((b, s_q, h_q, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((b, s_q, h_q), dtype=torch.float32, device=dev)
+
+    def step():
+        ops.mla_get_decode_metadata(t["seqlens"], b, s_q, h_q, 1, parts, meta, ns)
+        ops.mla_decode_fwd(t["q"], t["kcache"], ops.KV_BF16_PAGED, t["block_table"], t["seqlens"], w.scale,
+                           w.causal, meta, ns, out, lse, ws)
+        ops.mla_combine(ns, ws, b, s_q, h_q, parts, out, lse)
+
+    step()
+    torch.cuda.synchronize()
+    G.compare("graph-eager", out, lse, *oracle_dense(w))
+    ref_o, ref_l = out.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(0)
+        lse.fill_(0)
+        ws.fill_(0)
+        meta.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"replay {rep} differs from the eager step"
