@@ -82,8 +82,10 @@ typedef enum {
 } mla_status;
 
 typedef enum {
-  MLA_KV_BF16_PAGED = 0, /* kcache bf16 pages reached through block_table */
-  MLA_KV_FP8_PACKED = 1  /* the workspace written by mla_pack_selected_kv */
+  MLA_KV_BF16_PAGED = 0,  /* kcache bf16 pages reached through block_table */
+  MLA_KV_FP8_PACKED = 1,  /* the workspace written by mla_pack_selected_kv */
+  MLA_KV_FP8_INDEXED = 2  /* the FP8 record pool itself, records gathered by
+                             top-k index inside the decode (no pack) */
 } mla_kv_format;
 
 /* Text of the last error on the calling host thread ("" if none).  The
@@ -131,15 +133,29 @@ size_t mla_packed_kv_workspace_size(int batch, int s_q, int topk_capacity);
 int mla_get_decode_metadata(const int32_t* seqlens, int batch, int s_q, int h_q, int h_kv, int num_parts,
                             int32_t* sched_meta, int32_t* num_splits, void* stream);
 
-/* Decode (device).  Launches num_parts x ceil(s_q*h_q / 128) workgroups; each
- * walks its partition's pages with an online softmax and writes either the
- * final out/lse rows (request not split) or a split partial into `workspace`.
- * mla_combine must follow on the same stream to finish split requests.
+/* Decode (device).  Launches num_parts x ceil(s_q*h_q / R) workgroups (R = 16,
+ * 32 or 64 query rows per workgroup); each walks its partition's pages with an
+ * online softmax and writes either the final out/lse rows (request not split)
+ * or a split partial into `workspace`.  mla_combine must follow on the same
+ * stream to finish split requests.
  *   q (device) bf16 [batch][s_q][h_q][576]
  *   kv (device): MLA_KV_BF16_PAGED -> kcache bf16 [num_pages][64][1][576];
  *                MLA_KV_FP8_PACKED -> packed workspace of mla_pack_selected_kv
  *                (then block_table/max_pages/num_pages are ignored, seqlens is
- *                topk_length, s_q must be 1, h_q must be 64 or 128, no causal)
+ *                topk_length, s_q must be 1, h_q must be 64 or 128, no causal);
+ *                MLA_KV_FP8_INDEXED -> kcache_fp8 uint8 [num_pages][64][1][656],
+ *                the pool the pack reads: the decode gathers the selected
+ *                records itself ("native" sparse decode, the fallback when the
+ *                pack cannot be hidden: "[SM90] Add packed selected-KV sparse
+ *                decode", FlashMLA PR 200, Motivation and Runtime follow-up).
+ *                block_table is then the int32 [batch][s_q][topk_capacity]
+ *                top-k physical token ids (page = id / 64, slot = id % 64; only
+ *                k < topk_length[r] is read), max_pages is ignored, seqlens is
+ *                topk_length, and the same scope as the packed path applies.
+ *                Same arithmetic as the packed path: bitwise equal results for
+ *                ids inside the pool.  An id outside it is flagged (bit 1) and
+ *                read as id 0 (the pack writes a zero record instead); the
+ *                output of a flagged call is not meaningful.
  *   block_table (device) int32 [batch][max_pages], seqlens (device) int32 [batch]
  *   softmax_scale: multiplies q.k (e.g. 576^-0.5); must be finite and > 0, else
  *                  MLA_ERR_INVALID_ARGUMENT; causal: 0/1

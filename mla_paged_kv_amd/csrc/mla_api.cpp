@@ -76,11 +76,11 @@ int check_shape(int batch, int s_q, int h_q, int h_kv, int kv_format) {
   if (h_kv != 1) return fail(MLA_ERR_UNSUPPORTED, "h_kv %d: only one latent KV head is supported", h_kv);
   if (h_q % 16 != 0 || h_q > 128) return fail(MLA_ERR_UNSUPPORTED, "h_q %d: must be a multiple of 16 and <= 128", h_q);
   if ((int64_t)s_q * h_q > MLA_MAX_ROWS) return fail(MLA_ERR_UNSUPPORTED, "s_q * h_q = %d above %d", s_q * h_q, MLA_MAX_ROWS);
-  if (kv_format != MLA_KV_BF16_PAGED && kv_format != MLA_KV_FP8_PACKED)
+  if (kv_format != MLA_KV_BF16_PAGED && kv_format != MLA_KV_FP8_PACKED && kv_format != MLA_KV_FP8_INDEXED)
     return fail(MLA_ERR_UNSUPPORTED, "kv_format %d unknown", kv_format);
-  if (kv_format == MLA_KV_FP8_PACKED) {
-    if (s_q != 1) return fail(MLA_ERR_UNSUPPORTED, "packed FP8 decode supports s_q = 1 only (got %d)", s_q);
-    if (h_q != 64 && h_q != 128) return fail(MLA_ERR_UNSUPPORTED, "packed FP8 decode supports h_q in {64, 128} (got %d)", h_q);
+  if (kv_format != MLA_KV_BF16_PAGED) {
+    if (s_q != 1) return fail(MLA_ERR_UNSUPPORTED, "sparse FP8 decode supports s_q = 1 only (got %d)", s_q);
+    if (h_q != 64 && h_q != 128) return fail(MLA_ERR_UNSUPPORTED, "sparse FP8 decode supports h_q in {64, 128} (got %d)", h_q);
   }
   return MLA_OK;
 }
@@ -121,7 +121,7 @@ int mla_decode_num_parts(int batch, int s_q, int h_q, int h_kv, int kv_format, i
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail(e, "device query");
-  e = mla::decode_occupancy(kv_format == MLA_KV_FP8_PACKED, s_q * h_q, &wgs);
+  e = mla::decode_occupancy(kv_format, s_q * h_q, &wgs);
   if (e != hipSuccess) return hip_fail(e, "occupancy query");
   if (wgs < 1) return fail(MLA_ERR_HIP, "decode kernel does not fit on a CU");
   return mla_plan_num_parts(batch, s_q, h_q, kv_format, cus, wgs, num_parts_out);
@@ -160,11 +160,16 @@ int mla_decode_fwd(const void* q, const void* kv, int kv_format, int64_t num_pag
     return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
   int st = check_shape(batch, s_q, h_q, h_kv, kv_format);
   if (st) return st;
-  const bool fp8 = kv_format == MLA_KV_FP8_PACKED;
+  const bool fp8 = kv_format != MLA_KV_BF16_PAGED;
   if (fp8) {
     if (topk_capacity < mla::kPage || topk_capacity % mla::kPage != 0)
       return fail(MLA_ERR_UNSUPPORTED, "topk_capacity %d must be a positive multiple of 64", topk_capacity);
-    if (causal) return fail(MLA_ERR_UNSUPPORTED, "packed FP8 decode has no causal mask");
+    if (causal) return fail(MLA_ERR_UNSUPPORTED, "sparse FP8 decode has no causal mask");
+    if (kv_format == MLA_KV_FP8_INDEXED) {
+      if (!block_table) return fail(MLA_ERR_INVALID_ARGUMENT, "indices (block_table argument) is NULL");
+      if (num_pages < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "num_pages %lld < 1", (long long)num_pages);
+      if (num_pages > INT64_MAX / (mla::kPage * mla::kRecBytes)) return fail(MLA_ERR_UNSUPPORTED, "num_pages too large");
+    }
   } else {
     if (!block_table) return fail(MLA_ERR_INVALID_ARGUMENT, "block_table is NULL");
     if (max_pages < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "max_pages %d < 1", max_pages);
@@ -204,7 +209,10 @@ int mla_decode_fwd(const void* q, const void* kv, int kv_format, int64_t num_pag
   a.slots = slots_for(batch, num_parts);
   a.part_o = (float*)workspace;
   a.part_lse = a.part_o + (size_t)a.slots * a.M * mla::kDV;
-  hipError_t e = mla::launch_decode(a, fp8, (hipStream_t)stream);
+  const int kind = kv_format == MLA_KV_FP8_PACKED    ? mla::kDecodeFp8Packed
+                   : kv_format == MLA_KV_FP8_INDEXED ? mla::kDecodeFp8Indexed
+                                                     : mla::kDecodeBf16;
+  hipError_t e = mla::launch_decode(a, kind, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
 }

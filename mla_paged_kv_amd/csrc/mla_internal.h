@@ -24,9 +24,9 @@ constexpr int kErrMeta = 8;
 
 struct DecodeArgs {
   const uint16_t* q;          // bf16 bits [batch][s_q][h_q][576]
-  const uint8_t* kv;          // bf16 pages, or packed FP8 records
+  const uint8_t* kv;          // bf16 pages, packed FP8 records, or the FP8 record pool
   int64_t num_pages;
-  const int32_t* block_table; // [batch][max_pages]
+  const int32_t* block_table; // [batch][max_pages]; FP8 indexed: top-k token ids [batch][s_q][cap]
   int max_pages;
   const int32_t* seqlens;     // [batch] (packed: topk_length)
   int cap;                    // packed: top-k capacity (multiple of 64)
@@ -48,12 +48,14 @@ int decode_row_blocks_per_wg(int M);
 
 hipError_t launch_sched(const int32_t* lengths, int batch, int num_parts, int32_t* meta, int32_t* num_splits,
                         hipStream_t stream);
-hipError_t launch_decode(const DecodeArgs& a, bool fp8, hipStream_t stream);
+// Decode kernel family: bf16 pages, FP8 packed workspace, FP8 pool gathered by index.
+enum DecodeKind { kDecodeBf16 = 0, kDecodeFp8Packed = 1, kDecodeFp8Indexed = 2 };
+hipError_t launch_decode(const DecodeArgs& a, int kind, hipStream_t stream);
 hipError_t launch_combine(const int32_t* num_splits, const float* part_o, const float* part_lse, int batch, int M,
                           int slots, uint16_t* out, float* lse, hipStream_t stream);
 hipError_t launch_pack(const uint8_t* kcache, int64_t num_pages, const int32_t* indices, const int32_t* topk_length,
                        int batch, int s_q, int cap, uint8_t* ws, hipStream_t stream);
-hipError_t decode_occupancy(bool fp8, int M, int* wgs_per_cu);
+hipError_t decode_occupancy(int kind, int M, int* wgs_per_cu);
 hipError_t read_and_clear_error_flags(int* flags, hipStream_t stream);
 
 }  // namespace mla

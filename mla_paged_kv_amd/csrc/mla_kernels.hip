@@ -418,6 +418,39 @@ struct TileLoader<true> {
   }
 };
 
+// FP8 records gathered by index from the paged pool (no pack): record j of the
+// tile of keys [key0, key0 + 32) is kcache_fp8[idx / 64][idx % 64] with
+// idx = indices[r][key0 + j].  One wave-wide load per record (lanes 0..40 each
+// move one 16-byte chunk of the 656 bytes; the others idle), so the record's
+// base address is wave-uniform and comes from a scalar load of its index; wave w
+// moves records w, w + 4, ..., w + 28 into the same raw tile layout the packed
+// loader produces.  Keys past topk_length load record 0 (they are masked); an
+// index of the valid prefix outside the pool is flagged and replaced by 0.
+constexpr int kIdxLoadsPerWave = kTK / 4;  // 8
+struct IndexedLoader {
+  __device__ void init(int, int) {}
+  __device__ void issue(const DecodeArgs& a, int r, int key0, LDS_AS uint8_t* smem, int st, int w) const {
+    const int l = threadIdx.x & 63;
+    const int n = ld_const(a.seqlens, r);
+    const int64_t limit = a.num_pages * kPage;
+    LDS_AS uint8_t* dst = smem + kOffRaw + st * kRawTileBytes;
+#pragma unroll
+    for (int k = 0; k < kIdxLoadsPerWave; ++k) {
+      const int j = w + 4 * k;
+      int64_t idx = 0;
+      if (key0 + j < n) {
+        idx = ld_const(a.block_table, (int64_t)r * a.cap + key0 + j);
+        if (idx < 0 || idx >= limit) {
+          if (l == 0) atomicOr(&g_error_flags, kErrIndex);
+          idx = 0;
+        }
+      }
+      const uint64_t base = uniform_u64((uint64_t)(uintptr_t)a.kv + (uint64_t)idx * kRecBytes);
+      if (l < kRecBytes / 16) load_lds16_s(base, 16u * (uint32_t)l, dst + j * kRecBytes);
+    }
+  }
+};
+
 // Widen a raw FP8 tile into the swizzled bf16 tile: NoPE bytes E4M3 -> bf16 (exact:
 // every E4M3 value is a bf16 value; the per-block fp32 scales are applied later,
 // in fp32, to the scores and to P), RoPE copied.  Rows >= nvalid become zero.
@@ -467,8 +500,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // One workgroup: the 16*RB query rows of row block blockIdx.y, over the KV range
 // of partition blockIdx.x.  Wave w computes scores for rows [16w, 16w+16) (if
 // w < RB) and accumulates output columns [128w, 128w+128) for all rows.
-template <int RB, bool FP8>
+template <int RB, bool FP8, bool IDX = false>
 __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a) {
+  static_assert(FP8 || !IDX, "indexed gather is an FP8 mode");
   constexpr int MB = 16 * RB;  // rows per workgroup
   static_assert(MB <= kMaxRowsPerWG, "row block");
   __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[lds_bytes(FP8)];
@@ -494,7 +528,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
     return;
   }
 
-  TileLoader<FP8> loader;
+  std::conditional_t<IDX, IndexedLoader, TileLoader<FP8>> loader;
   loader.init(w, l);
 
   // QK^T: per-lane K-operand byte offsets for even/odd 32-dim k-steps (see tile_off):
@@ -561,7 +595,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
 
     for (int tile = 0; tile < ntile; ++tile) {
       // own loads of this tile done (later tiles may stay in flight) ...
-      constexpr int LPW = FP8 ? kRawLoadsPerWave : kLoadsPerWave;
+      constexpr int LPW = IDX ? kIdxLoadsPerWave : (FP8 ? kRawLoadsPerWave : kLoadsPerWave);
       if (tile + 2 < ntile) wait_vmcnt<2 * LPW>();
       else if (tile + 1 < ntile) wait_vmcnt<LPW>();
       else wait_vmcnt<0>();
@@ -1218,38 +1252,43 @@ int decode_row_blocks_per_wg(int M) {
   return 4;
 }
 
-template <int RB, bool FP8>
-static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+template <int RB>
+static hipError_t launch_decode_t(const DecodeArgs& a, int kind, hipStream_t stream) {
   const int MB = 16 * RB;
   dim3 grid(a.num_parts, (a.M + MB - 1) / MB);
-  if constexpr (FP8)
-    hipLaunchKernelGGL((decode_kernel<RB, true>), grid, dim3(kDecodeThreads), 0, stream, a);
+  if (kind == kDecodeFp8Packed)
+    hipLaunchKernelGGL((decode_kernel<RB, true, false>), grid, dim3(kDecodeThreads), 0, stream, a);
+  else if (kind == kDecodeFp8Indexed)
+    hipLaunchKernelGGL((decode_kernel<RB, true, true>), grid, dim3(kDecodeThreads), 0, stream, a);
   else
     hipLaunchKernelGGL((decode_ws_kernel<RB>), grid, dim3(kWsThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs& a, bool fp8, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, int kind, hipStream_t stream) {
   switch (decode_row_blocks_per_wg(a.M)) {
-    case 1: return fp8 ? launch_decode_t<1, true>(a, stream) : launch_decode_t<1, false>(a, stream);
-    case 2: return fp8 ? launch_decode_t<2, true>(a, stream) : launch_decode_t<2, false>(a, stream);
-    default: return fp8 ? launch_decode_t<4, true>(a, stream) : launch_decode_t<4, false>(a, stream);
+    case 1: return launch_decode_t<1>(a, kind, stream);
+    case 2: return launch_decode_t<2>(a, kind, stream);
+    default: return launch_decode_t<4>(a, kind, stream);
   }
 }
 
-hipError_t decode_occupancy(bool fp8, int M, int* wgs_per_cu) {
+template <int RB>
+static hipError_t occupancy_t(int kind, int* n) {
+  if (kind == kDecodeFp8Packed)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_kernel<RB, true, false>, kDecodeThreads, 0);
+  if (kind == kDecodeFp8Indexed)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_kernel<RB, true, true>, kDecodeThreads, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_ws_kernel<RB>, kWsThreads, 0);
+}
+
+hipError_t decode_occupancy(int kind, int M, int* wgs_per_cu) {
   int n = 0;
   hipError_t e;
   switch (decode_row_blocks_per_wg(M)) {
-    case 1: e = fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<1, true>, kDecodeThreads, 0)
-                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_ws_kernel<1>, kWsThreads, 0);
-      break;
-    case 2: e = fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<2, true>, kDecodeThreads, 0)
-                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_ws_kernel<2>, kWsThreads, 0);
-      break;
-    default: e = fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<4, true>, kDecodeThreads, 0)
-                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_ws_kernel<4>, kWsThreads, 0);
-      break;
+    case 1: e = occupancy_t<1>(kind, &n); break;
+    case 2: e = occupancy_t<2>(kind, &n); break;
+    default: e = occupancy_t<4>(kind, &n); break;
   }
   *wgs_per_cu = n;
   return e;

@@ -33,6 +33,7 @@ MLA_ERR_WORKSPACE_TOO_SMALL = -3
 MLA_ERR_HIP = -4
 KV_BF16_PAGED = 0
 KV_FP8_PACKED = 1
+KV_FP8_INDEXED = 2
 D_QK, D_V, PAGE, REC_BYTES = 576, 512, 64, 656
 SCHED_META_INTS = 8
 
@@ -149,6 +150,19 @@ def mla_decode_fwd(q, kv, kv_format, block_table, seqlens, softmax_scale, causal
         if block_table.dim() != 2 or block_table.shape[0] != b:
             raise ValueError("block_table must be [batch, max_pages]")
         num_pages, max_pages = kv.shape[0], block_table.shape[1]
+    elif kv_format == KV_FP8_INDEXED:
+        # the FP8 record pool itself; block_table carries the top-k token ids
+        _need(kv, "kcache_fp8", torch.uint8)
+        if tuple(kv.shape[1:]) != (PAGE, 1, REC_BYTES):
+            raise ValueError(f"kcache_fp8 shape {tuple(kv.shape)}, expected [pages, 64, 1, 656]")
+        _need(block_table, "indices", torch.int32)
+        if block_table.dim() != 3 or block_table.shape[:2] != (b, s_q):
+            raise ValueError("indices must be [batch, s_q, topk_capacity]")
+        if topk_capacity == 0:
+            topk_capacity = block_table.shape[2]
+        if topk_capacity != block_table.shape[2]:
+            raise ValueError(f"topk_capacity {topk_capacity} != indices.shape[2] {block_table.shape[2]}")
+        num_pages, max_pages = kv.shape[0], 0
     else:
         _need(kv, "packed workspace", torch.uint8)
         num_pages, max_pages = 0, 0
@@ -159,7 +173,7 @@ def mla_decode_fwd(q, kv, kv_format, block_table, seqlens, softmax_scale, causal
     _need(lse, "lse", torch.float32, (b, s_q, h_q))
     _need(workspace, "workspace", torch.uint8)
     _check(_lib.mla_decode_fwd(
-        _ptr(q), _ptr(kv), kv_format, num_pages, _ptr(block_table) if kv_format == KV_BF16_PAGED else None,
+        _ptr(q), _ptr(kv), kv_format, num_pages, _ptr(block_table) if kv_format != KV_FP8_PACKED else None,
         max_pages, _ptr(seqlens), topk_capacity, b, s_q, h_q, 1, float(softmax_scale), int(bool(causal)),
         _ptr(sched_meta), _ptr(num_splits), sched_meta.shape[0], _ptr(out), _ptr(lse), _ptr(workspace),
         workspace.numel(), _stream(stream)))

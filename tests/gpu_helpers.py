@@ -51,6 +51,17 @@ def run_sparse(w, t=None, num_parts=None):
     return out, lse, ws, plan
 
 
+def run_sparse_indexed(w, t=None, num_parts=None):
+    """Sparse FP8 decode straight from the record pool (records gathered by
+    top-k id inside the decode, no pack)."""
+    t = t or dev_tensors(w)
+    plan = ops.DecodePlan(t["seqlens"], w.s_q, w.h_q, ops.KV_FP8_INDEXED, num_parts=num_parts or w.num_parts)
+    out, lse = ops.mla_decode(t["q"], t["kcache_rec"], t["indices"], t["seqlens"], w.scale, False, plan=plan,
+                              kv_format=ops.KV_FP8_INDEXED, topk_capacity=w.topk_capacity)
+    torch.cuda.synchronize()
+    return out, lse, plan
+
+
 def to_np(out, lse):
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 

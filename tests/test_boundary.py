@@ -86,6 +86,13 @@ def decode_call(**kw):
     (dict(fmt=ops.KV_FP8_PACKED, cap=2000, h_q=64), ops.MLA_ERR_UNSUPPORTED),
     (dict(fmt=ops.KV_FP8_PACKED, cap=2048, h_q=64, s_q=2), ops.MLA_ERR_UNSUPPORTED),
     (dict(fmt=ops.KV_FP8_PACKED, cap=2048, h_q=64, causal=1), ops.MLA_ERR_UNSUPPORTED),
+    (dict(fmt=ops.KV_FP8_INDEXED, cap=2048, h_q=96), ops.MLA_ERR_UNSUPPORTED),
+    (dict(fmt=ops.KV_FP8_INDEXED, cap=100, h_q=64), ops.MLA_ERR_UNSUPPORTED),
+    (dict(fmt=ops.KV_FP8_INDEXED, cap=2048, h_q=128, s_q=2), ops.MLA_ERR_UNSUPPORTED),
+    (dict(fmt=ops.KV_FP8_INDEXED, cap=2048, h_q=128, causal=1), ops.MLA_ERR_UNSUPPORTED),
+    (dict(fmt=ops.KV_FP8_INDEXED, cap=2048, h_q=128, bt=NULL), ops.MLA_ERR_INVALID_ARGUMENT),
+    (dict(fmt=ops.KV_FP8_INDEXED, cap=2048, h_q=128, num_pages=0), ops.MLA_ERR_INVALID_ARGUMENT),
+    (dict(fmt=ops.KV_FP8_INDEXED, cap=2048, h_q=128, num_pages=1 << 60), ops.MLA_ERR_UNSUPPORTED),
     (dict(batch=0), ops.MLA_ERR_INVALID_ARGUMENT),
     (dict(batch=9000), ops.MLA_ERR_UNSUPPORTED),
     (dict(s_q=0), ops.MLA_ERR_INVALID_ARGUMENT),

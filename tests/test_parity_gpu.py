@@ -233,6 +233,51 @@ def test_config_c5():
     G.compare("c5", out, lse, *oracle_sparse(w))
 
 
+# ----------------------------------------------------------------------------- FP8 decode gathering by index
+
+@pytest.mark.parametrize("case", SPARSE, ids=[c[0] for c in SPARSE])
+def test_fp8_indexed_decode(case):
+    """The decode that gathers the selected records itself matches the oracle and,
+    bit for bit, the pack + packed decode (same arithmetic, same split)."""
+    name, seed, b, h, cap, topk, ctx, parts = case
+    G.say(f"fp8 indexed {name}")
+    w = W.sparse_workload(name, seed, b, h, cap, topk, context=ctx, num_parts=parts)
+    t = G.dev_tensors(w)
+    out, lse, plan = G.run_sparse_indexed(w, t)
+    G.compare(name, out, lse, *oracle_sparse(w))
+    out_p, lse_p, _, plan_p = G.run_sparse(w, t)
+    assert plan.num_parts == plan_p.num_parts
+    assert torch.equal(out, out_p) and torch.equal(lse, lse_p)
+    assert ops.mla_read_device_errors() == 0
+
+
+def test_fp8_indexed_config_c5():
+    G.say("config c5 indexed")
+    w = W.config("c5")
+    t = G.dev_tensors(w)
+    out, lse, plan = G.run_sparse_indexed(w, t)
+    G.say(f"  num_parts={plan.num_parts}")
+    G.compare("c5-indexed", out, lse, *oracle_sparse(w))
+    out_p, lse_p, _, _ = G.run_sparse(w, t)
+    assert torch.equal(out, out_p) and torch.equal(lse, lse_p)
+
+
+def test_fp8_indexed_ignores_ids_past_topk_length():
+    """Ids at positions >= topk_length are never read: garbage there (even out of
+    the pool) changes nothing and raises no flag."""
+    G.say("fp8 indexed: garbage past topk_length")
+    w = W.sparse_workload("tail-garbage", 155, 2, 128, 256, [130, 31], context=2048)
+    t = G.dev_tensors(w)
+    out, lse, _ = G.run_sparse_indexed(w, t)
+    ops.mla_read_device_errors()
+    for r, n in enumerate(w.seqlens):
+        w.indices[r, :, n:] = -123456789
+    t2 = dict(t, indices=torch.from_numpy(w.indices).to("cuda:0"))
+    out2, lse2, _ = G.run_sparse_indexed(w, t2)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    assert ops.mla_read_device_errors() == 0
+
+
 # ----------------------------------------------------------------------------- device-side contract checks
 
 def test_out_of_range_page_sets_flag_without_fault():
@@ -244,6 +289,28 @@ def test_out_of_range_page_sets_flag_without_fault():
     flags = ops.mla_read_device_errors()
     assert flags & 1
     assert ops.mla_read_device_errors() == 0
+
+
+def test_out_of_range_topk_id_sets_flag_without_fault():
+    G.say("device flag: top-k id out of range (indexed decode)")
+    ops.mla_read_device_errors()  # clear
+    w = W.sparse_workload("badid", 156, 1, 64, 64, [40], context=512)
+    w.indices[0, 0, 3] = 64 * w.kcache_rec.shape[0] + 5  # one past-the-pool id in the valid prefix
+    w.indices[0, 0, 7] = -2
+    G.run_sparse_indexed(w)
+    flags = ops.mla_read_device_errors()
+    assert flags & 2
+    assert ops.mla_read_device_errors() == 0
+
+
+def test_topk_length_above_capacity_sets_flag_without_fault():
+    G.say("device flag: topk_length above capacity (indexed decode)")
+    ops.mla_read_device_errors()
+    w = W.sparse_workload("longlen", 157, 2, 64, 64, [64, 10], context=512)
+    t = G.dev_tensors(w)
+    t["seqlens"] = torch.tensor([1000, 10], dtype=torch.int32, device="cuda:0")
+    G.run_sparse_indexed(w, t)
+    assert ops.mla_read_device_errors() & 4
 
 
 # ----------------------------------------------------------------------------- HIP graph capture
