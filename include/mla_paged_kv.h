@@ -69,7 +69,7 @@ extern "C" {
 #define MLA_PAGE_TOKENS 64
 #define MLA_FP8_RECORD_BYTES 656
 #define MLA_SCHED_META_INTS 8
-#define MLA_MAX_ROWS 256       /* s_q * h_q per request */
+#define MLA_MAX_ROWS 2048      /* s_q * h_q per request */
 #define MLA_MAX_BATCH 65536
 #define MLA_MAX_PARTS 8192
 
@@ -142,7 +142,8 @@ int mla_get_decode_metadata(const int32_t* seqlens, int batch, int s_q, int h_q,
  *   kv (device): MLA_KV_BF16_PAGED -> kcache bf16 [num_pages][64][1][576];
  *                MLA_KV_FP8_PACKED -> packed workspace of mla_pack_selected_kv
  *                (then block_table/max_pages/num_pages are ignored, seqlens is
- *                topk_length, s_q must be 1, h_q must be 64 or 128, no causal);
+ *                topk_length, h_q must be 64 or 128, no causal; query token s of
+ *                request r attends to workspace row r * s_q + s);
  *                MLA_KV_FP8_INDEXED -> kcache_fp8 uint8 [num_pages][64][1][656],
  *                the pool the pack reads: the decode gathers the selected
  *                records itself ("native" sparse decode, the fallback when the
@@ -163,7 +164,7 @@ int mla_get_decode_metadata(const int32_t* seqlens, int batch, int s_q, int h_q,
  *     seqlens, batch and num_parts
  *   out (device) bf16 [batch][s_q][h_q][512], lse (device) fp32 [batch][s_q][h_q]
  *   workspace (device) of >= mla_decode_workspace_size(batch, s_q, h_q, num_parts)
- * Scope: h_kv = 1; h_q a multiple of 16 with h_q <= 128; s_q * h_q <= 256;
+ * Scope: h_kv = 1; h_q a multiple of 16 with h_q <= 128; s_q * h_q <= 2048;
  * gfx950 device. */
 int mla_decode_fwd(const void* q, const void* kv, int kv_format, int64_t num_pages, const int32_t* block_table,
                    int max_pages, const int32_t* seqlens, int topk_capacity, int batch, int s_q, int h_q, int h_kv,

@@ -79,7 +79,6 @@ int check_shape(int batch, int s_q, int h_q, int h_kv, int kv_format) {
   if (kv_format != MLA_KV_BF16_PAGED && kv_format != MLA_KV_FP8_PACKED && kv_format != MLA_KV_FP8_INDEXED)
     return fail(MLA_ERR_UNSUPPORTED, "kv_format %d unknown", kv_format);
   if (kv_format != MLA_KV_BF16_PAGED) {
-    if (s_q != 1) return fail(MLA_ERR_UNSUPPORTED, "sparse FP8 decode supports s_q = 1 only (got %d)", s_q);
     if (h_q != 64 && h_q != 128) return fail(MLA_ERR_UNSUPPORTED, "sparse FP8 decode supports h_q in {64, 128} (got %d)", h_q);
   }
   return MLA_OK;

@@ -420,18 +420,20 @@ struct TileLoader<true> {
 
 // FP8 records gathered by index from the paged pool (no pack): record j of the
 // tile of keys [key0, key0 + 32) is kcache_fp8[idx / 64][idx % 64] with
-// idx = indices[r][key0 + j].  One wave-wide load per record (lanes 0..40 each
-// move one 16-byte chunk of the 656 bytes; the others idle), so the record's
-// base address is wave-uniform and comes from a scalar load of its index; wave w
-// moves records w, w + 4, ..., w + 28 into the same raw tile layout the packed
-// loader produces.  Keys past topk_length load record 0 (they are masked); an
-// index of the valid prefix outside the pool is flagged and replaced by 0.
+// idx = indices[row][key0 + j] (row = r * s_q + s for query token s of request
+// r).  One wave-wide load per record (lanes 0..40 each move one 16-byte chunk
+// of the 656 bytes; the others idle), so the record's base address is
+// wave-uniform and comes from a scalar load of its index; wave w moves records
+// w, w + 4, ..., w + 28 into the same raw tile layout the packed loader
+// produces.  Keys past the request's top-k length `n` (set per request, already
+// clamped to the capacity) load record 0 (they are masked); an index of the
+// valid prefix outside the pool is flagged and replaced by 0.
 constexpr int kIdxLoadsPerWave = kTK / 4;  // 8
 struct IndexedLoader {
+  int n = 0;
   __device__ void init(int, int) {}
-  __device__ void issue(const DecodeArgs& a, int r, int key0, LDS_AS uint8_t* smem, int st, int w) const {
+  __device__ void issue(const DecodeArgs& a, int row, int key0, LDS_AS uint8_t* smem, int st, int w) const {
     const int l = threadIdx.x & 63;
-    const int n = ld_const(a.seqlens, r);
     const int64_t limit = a.num_pages * kPage;
     LDS_AS uint8_t* dst = smem + kOffRaw + st * kRawTileBytes;
 #pragma unroll
@@ -439,7 +441,7 @@ struct IndexedLoader {
       const int j = w + 4 * k;
       int64_t idx = 0;
       if (key0 + j < n) {
-        idx = ld_const(a.block_table, (int64_t)r * a.cap + key0 + j);
+        idx = ld_const(a.block_table, (int64_t)row * a.cap + key0 + j);
         if (idx < 0 || idx >= limit) {
           if (l == 0) atomicOr(&g_error_flags, kErrIndex);
           idx = 0;
@@ -548,6 +550,11 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
       if (tid == 0) atomicOr(&g_error_flags, kErrSeqlen);
       seqlen = seqlen < 0 ? 0 : (FP8 ? a.cap : a.max_pages * kPage);
     }
+    // FP8: the selected keys of query token s of request r are row r * s_q + s of
+    // the packed workspace (or of the id lists); all rows of this workgroup
+    // belong to one token, as 16 * RB divides h_q there
+    const int lrow = FP8 ? r * a.s_q + (rbk * MB) / a.h_q : r;
+    if constexpr (IDX) loader.n = seqlen;
     const int nblk = (seqlen + kPage - 1) / kPage;
     const int blk0 = (r == begin_req) ? begin_blk : 0;
     const int blk1 = (r == end_req) ? end_blk : nblk;
@@ -591,7 +598,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
     // ---- pipeline prologue: tiles 0 .. kStages-2
 #pragma unroll
     for (int tt = 0; tt < kStages - 1; ++tt)
-      if (tt < ntile) loader.issue(a, r, t0 + tt * kTK, smem, tt, w);
+      if (tt < ntile) loader.issue(a, lrow, t0 + tt * kTK, smem, tt, w);
 
     for (int tile = 0; tile < ntile; ++tile) {
       // own loads of this tile done (later tiles may stay in flight) ...
@@ -602,7 +609,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a)
       // ... and everyone's, and every wave is past PV of the previous tile
       sync_lds();
       if (tile + kStages - 1 < ntile)
-        loader.issue(a, r, t0 + (tile + kStages - 1) * kTK, smem, (tile + kStages - 1) % kStages, w);
+        loader.issue(a, lrow, t0 + (tile + kStages - 1) * kTK, smem, (tile + kStages - 1) % kStages, w);
 
       const int key0 = t0 + tile * kTK;
       const int nvalid = min(kTK, t1 - key0);

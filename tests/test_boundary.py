@@ -80,15 +80,15 @@ def decode_call(**kw):
     (dict(h_kv=2), ops.MLA_ERR_UNSUPPORTED),
     (dict(h_q=17), ops.MLA_ERR_UNSUPPORTED),
     (dict(h_q=144), ops.MLA_ERR_UNSUPPORTED),
-    (dict(s_q=3, h_q=128), ops.MLA_ERR_UNSUPPORTED),      # 384 rows > 256
+    (dict(s_q=17, h_q=128), ops.MLA_ERR_UNSUPPORTED),     # 2176 rows > 2048
     (dict(fmt=7), ops.MLA_ERR_UNSUPPORTED),
     (dict(fmt=ops.KV_FP8_PACKED, cap=2048, h_q=96), ops.MLA_ERR_UNSUPPORTED),
     (dict(fmt=ops.KV_FP8_PACKED, cap=2000, h_q=64), ops.MLA_ERR_UNSUPPORTED),
-    (dict(fmt=ops.KV_FP8_PACKED, cap=2048, h_q=64, s_q=2), ops.MLA_ERR_UNSUPPORTED),
+    (dict(fmt=ops.KV_FP8_PACKED, cap=2048, h_q=128, s_q=17), ops.MLA_ERR_UNSUPPORTED),
     (dict(fmt=ops.KV_FP8_PACKED, cap=2048, h_q=64, causal=1), ops.MLA_ERR_UNSUPPORTED),
     (dict(fmt=ops.KV_FP8_INDEXED, cap=2048, h_q=96), ops.MLA_ERR_UNSUPPORTED),
     (dict(fmt=ops.KV_FP8_INDEXED, cap=100, h_q=64), ops.MLA_ERR_UNSUPPORTED),
-    (dict(fmt=ops.KV_FP8_INDEXED, cap=2048, h_q=128, s_q=2), ops.MLA_ERR_UNSUPPORTED),
+    (dict(fmt=ops.KV_FP8_INDEXED, cap=2048, h_q=64, s_q=33), ops.MLA_ERR_UNSUPPORTED),
     (dict(fmt=ops.KV_FP8_INDEXED, cap=2048, h_q=128, causal=1), ops.MLA_ERR_UNSUPPORTED),
     (dict(fmt=ops.KV_FP8_INDEXED, cap=2048, h_q=128, bt=NULL), ops.MLA_ERR_INVALID_ARGUMENT),
     (dict(fmt=ops.KV_FP8_INDEXED, cap=2048, h_q=128, num_pages=0), ops.MLA_ERR_INVALID_ARGUMENT),

@@ -65,6 +65,9 @@ DENSE_SMALL = [
     ("causal-sq2-h64-p1", 111, 2, 2, 64, [2, 95], 4, True, 1),
     ("causal-sq4-h64", 112, 2, 4, 64, [3, 300], 8, True, 6),
     ("noncausal-sq2-h128", 113, 2, 2, 128, [250, 64], 6, False, None),
+    ("causal-sq4-h128", 114, 2, 4, 128, [4, 700], 12, True, None),        # 512 rows per request
+    ("causal-sq16-h128-p3", 115, 1, 16, 128, [600], 10, True, 3),         # 2048 rows, the row cap
+    ("causal-sq8-h48", 116, 2, 8, 48, [8, 200], 6, True, None),           # rows not a multiple of 64
 ]
 
 
@@ -212,6 +215,33 @@ SPARSE = [
     ("tails-h128", 153, 3, 128, 512, [400, 17, 512], 8192, 7),
     ("empty-h64", 154, 2, 64, 128, [0, 77], 1024, None),
 ]
+
+
+# several query tokens per request, each with its own top-k list (workspace row r * s_q + s)
+SPARSE_MULTI = [
+    ("sq2-h128", 158, 2, 128, 256, [256, 100], 2048, 2, None),
+    ("sq4-h64-tails", 159, 3, 64, 128, [128, 70, 1], 1024, 4, None),
+    ("sq8-h64-p3", 160, 2, 64, 192, [150, 192], 4096, 8, 3),
+    ("sq16-h128", 161, 2, 128, 128, [128, 90], 1024, 16, None),
+]
+
+
+@pytest.mark.parametrize("case", SPARSE_MULTI, ids=[c[0] for c in SPARSE_MULTI])
+def test_fp8_multi_token(case):
+    """Packed and by-index sparse decode with s_q > 1 against the oracle, and
+    bitwise against each other."""
+    name, seed, b, h, cap, topk, ctx, s_q, parts = case
+    G.say(f"fp8 multi-token {name}")
+    w = W.sparse_workload(name, seed, b, h, cap, topk, context=ctx, s_q=s_q, num_parts=parts)
+    t = G.dev_tensors(w)
+    ref = oracle_sparse(w)
+    out_p, lse_p, ws, _ = G.run_sparse(w, t)
+    assert np.array_equal(ws.cpu().numpy(), O.pack_selected_kv(w.kcache_rec, w.indices, w.seqlens).reshape(-1))
+    G.compare(name + "-packed", out_p, lse_p, *ref)
+    out_i, lse_i, _ = G.run_sparse_indexed(w, t)
+    G.compare(name + "-indexed", out_i, lse_i, *ref)
+    assert torch.equal(out_p, out_i) and torch.equal(lse_p, lse_i)
+    assert ops.mla_read_device_errors() == 0
 
 
 @pytest.mark.parametrize("case", SPARSE, ids=[c[0] for c in SPARSE])
