@@ -194,6 +194,42 @@ int mla_pack_selected_kv(const void* kcache_fp8, int64_t num_pages, const int32_
                          const int32_t* topk_length, int batch, int s_q, int topk_capacity, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* Current-token patch (device).  Packing ahead of attention (on another
+ * stream, during preceding work) reads the pool before the current step's KV
+ * is written; afterwards this call overwrites every selected slot that refers
+ * to one of the changed tokens: for every row = r * s_q + i and slot
+ * k < topk_length[r] with indices[r][i][k] == new_ids[r][j] for some j < n_new,
+ * ws[row][k / 64][k % 64] = the record of that id in kcache_fp8.  If only the
+ * listed records changed since the pack, the workspace then equals a fresh
+ * pack of the current pool byte for byte.  ("Runtime follow-up", FlashMLA PR
+ * 200: pack historical records early into caller-managed storage, overwrite
+ * any selected current-token record once its KV is available, for example by
+ * a scatter, then synchronise the packing stream with attention.)
+ *   kcache_fp8, indices, topk_length, workspace: as for mla_pack_selected_kv
+ *     (same batch, s_q, topk_capacity; workspace written by that pack);
+ *   new_ids (device) int32 [batch][n_new]: the physical token ids whose
+ *     records changed, per request; entries < 0 are ignored; a matching id
+ *     outside [0, num_pages * 64) is flagged (bit 1) and not copied;
+ *   n_new in [1, 64].
+ * The pack must have completed (e.g. an event recorded after it on its
+ * stream, waited on by `stream`) and the new records must be written before
+ * this call runs on `stream`. */
+int mla_patch_packed_kv(const void* kcache_fp8, int64_t num_pages, const int32_t* indices,
+                        const int32_t* topk_length, int batch, int s_q, int topk_capacity, const int32_t* new_ids,
+                        int n_new, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Sparse path choice (host).  *kv_format_out = MLA_KV_FP8_PACKED when the
+ * pack can be hidden (pack_hidden != 0: the caller has an overlap window for
+ * mla_pack_selected_kv) and mla_packed_kv_workspace_size(batch, s_q,
+ * topk_capacity) <= workspace_budget_bytes; otherwise MLA_KV_FP8_INDEXED, the
+ * decode that gathers by id and needs no packed workspace.  ("Runtime
+ * follow-up", FlashMLA PR 200: choose the native path when the expected
+ * overlap is insufficient; enforce a workspace budget, about 1.281 MiB per
+ * query row at top-k 2048.)  An unhidden pack costs more than the packed
+ * decode saves at every shape measured here. */
+int mla_sparse_kv_format(int batch, int s_q, int topk_capacity, size_t workspace_budget_bytes, int pack_hidden,
+                         int* kv_format_out);
+
 /* Device-side violation flags accumulated by the kernels on the current
  * device since the last call (bit 0: page id out of range, bit 1: top-k id
  * out of range, bit 2: seqlen above max_pages * 64 or top-k length above the

@@ -257,6 +257,43 @@ int mla_pack_selected_kv(const void* kcache_fp8, int64_t num_pages, const int32_
   return ok();
 }
 
+int mla_patch_packed_kv(const void* kcache_fp8, int64_t num_pages, const int32_t* indices,
+                        const int32_t* topk_length, int batch, int s_q, int topk_capacity, const int32_t* new_ids,
+                        int n_new, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!kcache_fp8 || !indices || !topk_length || !new_ids || !workspace)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (batch < 1 || batch > MLA_MAX_BATCH) return fail(MLA_ERR_INVALID_ARGUMENT, "batch %d out of [1, %d]", batch, MLA_MAX_BATCH);
+  if (s_q < 1 || s_q > MLA_MAX_ROWS) return fail(MLA_ERR_INVALID_ARGUMENT, "s_q %d out of range", s_q);
+  if (num_pages < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "num_pages %lld < 1", (long long)num_pages);
+  if (num_pages > INT32_MAX / mla::kPage) return fail(MLA_ERR_UNSUPPORTED, "num_pages too large for int32 token ids");
+  if (n_new < 1 || n_new > mla::kPatchMaxNewIds)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "n_new %d out of [1, %d]", n_new, mla::kPatchMaxNewIds);
+  if (topk_capacity < mla::kPage || topk_capacity % mla::kPage != 0)
+    return fail(MLA_ERR_UNSUPPORTED, "topk_capacity %d must be a positive multiple of 64", topk_capacity);
+  if ((int64_t)batch * s_q > 65535 || topk_capacity / mla::kPage > 65535)
+    return fail(MLA_ERR_UNSUPPORTED, "grid too large");
+  const size_t need = mla_packed_kv_workspace_size(batch, s_q, topk_capacity);
+  if (workspace_bytes < need) return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "packed workspace %zu B < %zu B", workspace_bytes, need);
+  int st = check_device();
+  if (st) return st;
+  hipError_t e = mla::launch_patch((const uint8_t*)kcache_fp8, num_pages, indices, topk_length, new_ids, n_new, batch,
+                                   s_q, topk_capacity, (uint8_t*)workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "patch launch");
+  return ok();
+}
+
+int mla_sparse_kv_format(int batch, int s_q, int topk_capacity, size_t workspace_budget_bytes, int pack_hidden,
+                         int* kv_format_out) {
+  if (!kv_format_out) return fail(MLA_ERR_INVALID_ARGUMENT, "kv_format_out is NULL");
+  if (batch < 1 || batch > MLA_MAX_BATCH) return fail(MLA_ERR_INVALID_ARGUMENT, "batch %d out of [1, %d]", batch, MLA_MAX_BATCH);
+  if (s_q < 1 || s_q > MLA_MAX_ROWS) return fail(MLA_ERR_INVALID_ARGUMENT, "s_q %d out of range", s_q);
+  if (topk_capacity < mla::kPage || topk_capacity % mla::kPage != 0)
+    return fail(MLA_ERR_UNSUPPORTED, "topk_capacity %d must be a positive multiple of 64", topk_capacity);
+  const size_t need = mla_packed_kv_workspace_size(batch, s_q, topk_capacity);
+  *kv_format_out = (pack_hidden && need <= workspace_budget_bytes) ? MLA_KV_FP8_PACKED : MLA_KV_FP8_INDEXED;
+  return ok();
+}
+
 int mla_read_device_errors(int* flags_out, void* stream) {
   if (!flags_out) return fail(MLA_ERR_INVALID_ARGUMENT, "flags_out is NULL");
   int st = check_device();

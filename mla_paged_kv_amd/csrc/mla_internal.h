@@ -55,6 +55,10 @@ hipError_t launch_combine(const int32_t* num_splits, const float* part_o, const 
                           int slots, uint16_t* out, float* lse, hipStream_t stream);
 hipError_t launch_pack(const uint8_t* kcache, int64_t num_pages, const int32_t* indices, const int32_t* topk_length,
                        int batch, int s_q, int cap, uint8_t* ws, hipStream_t stream);
+hipError_t launch_patch(const uint8_t* kcache, int64_t num_pages, const int32_t* indices, const int32_t* topk_length,
+                        const int32_t* new_ids, int n_new, int batch, int s_q, int cap, uint8_t* ws,
+                        hipStream_t stream);
+constexpr int kPatchMaxNewIds = 64;
 hipError_t decode_occupancy(int kind, int M, int* wgs_per_cu);
 hipError_t read_and_clear_error_flags(int* flags, hipStream_t stream);
 

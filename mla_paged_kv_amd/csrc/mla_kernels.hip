@@ -1379,6 +1379,46 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ k
   }
 }
 
+// Current-token patch: one wave per (row, 64-slot tile).  Lane l tests slot
+// k = 64 tile + l of the row against the request's changed ids; the wave then
+// copies each matching record (lanes 0..40 move its 41 16-byte chunks).  Only
+// slots whose id matches are written, so the rest of the packed tile stays as
+// the pack left it.
+__global__ __launch_bounds__(64) void patch_kernel(const uint8_t* __restrict__ kcache, int64_t num_pages,
+                                                   const int32_t* __restrict__ indices,
+                                                   const int32_t* __restrict__ topk_length,
+                                                   const int32_t* __restrict__ new_ids, int n_new, int s_q, int cap,
+                                                   uint8_t* __restrict__ ws) {
+  constexpr int kChunksPerRec = kRecBytes / 16;  // 41
+  const int row = blockIdx.x;                    // r * s_q + i
+  const int k = blockIdx.y * kPage + (int)threadIdx.x;
+  const int r = row / s_q;
+  int n = ld_const(topk_length, r);
+  n = n < 0 ? 0 : (n > cap ? cap : n);  // the pack flags out-of-range lengths
+  int id = -1;
+  if (k < n) id = indices[(int64_t)row * cap + k];
+  bool hit = false;
+  if (id >= 0) {
+    for (int j = 0; j < n_new; ++j) hit |= id == ld_const(new_ids, (int64_t)r * n_new + j);
+  }
+  uint64_t m = __ballot(hit);
+  const int64_t limit = num_pages * kPage;
+  while (m) {
+    const int src_lane = __builtin_ctzll(m);
+    m &= m - 1;
+    const int sid = __builtin_amdgcn_readlane(id, src_lane);
+    if (sid >= limit) {  // id outside the pool (the pack flagged and zero-filled it)
+      if (threadIdx.x == 0) atomicOr(&g_error_flags, kErrIndex);
+      continue;
+    }
+    const int kk = blockIdx.y * kPage + src_lane;
+    if (threadIdx.x < kChunksPerRec) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(kcache + (int64_t)sid * kRecBytes + threadIdx.x * 16);
+      *reinterpret_cast<u32x4*>(ws + ((int64_t)row * cap + kk) * kRecBytes + threadIdx.x * 16) = v;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 hipError_t launch_sched(const int32_t* lengths, int batch, int num_parts, int32_t* meta, int32_t* num_splits,
                         hipStream_t stream) {
@@ -1398,6 +1438,15 @@ hipError_t launch_pack(const uint8_t* kcache, int64_t num_pages, const int32_t* 
                        int batch, int s_q, int cap, uint8_t* ws, hipStream_t stream) {
   dim3 grid(batch * s_q, cap / kPage);
   hipLaunchKernelGGL(pack_kernel, grid, dim3(256), 0, stream, kcache, num_pages, indices, topk_length, s_q, cap, ws);
+  return hipGetLastError();
+}
+
+hipError_t launch_patch(const uint8_t* kcache, int64_t num_pages, const int32_t* indices, const int32_t* topk_length,
+                        const int32_t* new_ids, int n_new, int batch, int s_q, int cap, uint8_t* ws,
+                        hipStream_t stream) {
+  dim3 grid(batch * s_q, cap / kPage);
+  hipLaunchKernelGGL(patch_kernel, grid, dim3(64), 0, stream, kcache, num_pages, indices, topk_length, new_ids, n_new,
+                     s_q, cap, ws);
   return hipGetLastError();
 }
 

@@ -51,6 +51,8 @@ _SIGS = {
                         _P, _P, _P, _sz, _P], _i32),
     "mla_combine": ([_P, _P, _sz, _i32, _i32, _i32, _i32, _P, _P, _P], _i32),
     "mla_pack_selected_kv": ([_P, _i64, _P, _P, _i32, _i32, _i32, _P, _sz, _P], _i32),
+    "mla_patch_packed_kv": ([_P, _i64, _P, _P, _i32, _i32, _i32, _P, _i32, _P, _sz, _P], _i32),
+    "mla_sparse_kv_format": ([_i32, _i32, _i32, _sz, _i32, _P], _i32),
     "mla_read_device_errors": ([_P, _P], _i32),
 }
 for _name, (_args, _res) in _SIGS.items():
@@ -202,6 +204,32 @@ def mla_pack_selected_kv(kcache_fp8, indices, topk_length, workspace=None, strea
     _check(_lib.mla_pack_selected_kv(_ptr(kcache_fp8), kcache_fp8.shape[0], _ptr(indices), _ptr(topk_length), b,
                                      s_q, cap, _ptr(workspace), workspace.numel(), _stream(stream)))
     return workspace
+
+
+def mla_patch_packed_kv(kcache_fp8, indices, topk_length, new_ids, workspace, stream=None):
+    """Overwrite the packed slots that select one of `new_ids` (int32 [batch, n_new])
+    with those records' current bytes."""
+    _need(kcache_fp8, "kcache_fp8", torch.uint8)
+    if tuple(kcache_fp8.shape[1:]) != (PAGE, 1, REC_BYTES):
+        raise ValueError(f"kcache_fp8 shape {tuple(kcache_fp8.shape)}, expected [pages, 64, 1, 656]")
+    _need(indices, "indices", torch.int32)
+    b, s_q, cap = indices.shape
+    _need(topk_length, "topk_length", torch.int32, (b,))
+    _need(new_ids, "new_ids", torch.int32)
+    if new_ids.dim() != 2 or new_ids.shape[0] != b:
+        raise ValueError("new_ids must be [batch, n_new]")
+    _need(workspace, "workspace", torch.uint8)
+    _check(_lib.mla_patch_packed_kv(_ptr(kcache_fp8), kcache_fp8.shape[0], _ptr(indices), _ptr(topk_length), b, s_q,
+                                    cap, _ptr(new_ids), new_ids.shape[1], _ptr(workspace), workspace.numel(),
+                                    _stream(stream)))
+    return workspace
+
+
+def mla_sparse_kv_format(batch, s_q, topk_capacity, workspace_budget_bytes, pack_hidden) -> int:
+    out = ctypes.c_int(-1)
+    _check(_lib.mla_sparse_kv_format(batch, s_q, topk_capacity, int(workspace_budget_bytes), int(bool(pack_hidden)),
+                                     ctypes.byref(out)))
+    return out.value
 
 
 def mla_read_device_errors(stream=None) -> int:

@@ -131,6 +131,44 @@ def test_metadata_and_combine_and_pack_fail_closed():
     assert lib.mla_decode_num_parts(1, 1, 128, 2, 0, ctypes.byref(out)) == ops.MLA_ERR_UNSUPPORTED
 
 
+def test_sparse_kv_format_policy():
+    need = ops.mla_packed_kv_workspace_size(8, 1, 2048)
+    assert need == 8 * 2048 * 656
+    assert ops.mla_sparse_kv_format(8, 1, 2048, need, True) == ops.KV_FP8_PACKED
+    assert ops.mla_sparse_kv_format(8, 1, 2048, need - 1, True) == ops.KV_FP8_INDEXED  # over the budget
+    assert ops.mla_sparse_kv_format(8, 1, 2048, 1 << 40, False) == ops.KV_FP8_INDEXED  # pack not hidden
+    assert ops.mla_sparse_kv_format(2, 4, 128, 1 << 40, True) == ops.KV_FP8_PACKED
+    out = ctypes.c_int(0)
+    assert lib.mla_sparse_kv_format(8, 1, 100, 1 << 40, 1, ctypes.byref(out)) == ops.MLA_ERR_UNSUPPORTED
+    assert lib.mla_sparse_kv_format(0, 1, 2048, 1 << 40, 1, ctypes.byref(out)) == ops.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_sparse_kv_format(8, 1, 2048, 1 << 40, 1, NULL) == ops.MLA_ERR_INVALID_ARGUMENT
+
+
+def patch_call(**kw):
+    args = dict(kv=FAKE, num_pages=16, idx=FAKE, tl=FAKE, batch=2, s_q=1, cap=128, ids=FAKE, n_new=1, ws=FAKE,
+                ws_bytes=1 << 40, stream=NULL)
+    args.update(kw)
+    return lib.mla_patch_packed_kv(args["kv"], args["num_pages"], args["idx"], args["tl"], args["batch"], args["s_q"],
+                                   args["cap"], args["ids"], args["n_new"], args["ws"], args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kv=NULL), ops.MLA_ERR_INVALID_ARGUMENT),
+    (dict(ids=NULL), ops.MLA_ERR_INVALID_ARGUMENT),
+    (dict(ws=NULL), ops.MLA_ERR_INVALID_ARGUMENT),
+    (dict(n_new=0), ops.MLA_ERR_INVALID_ARGUMENT),
+    (dict(n_new=65), ops.MLA_ERR_INVALID_ARGUMENT),
+    (dict(num_pages=0), ops.MLA_ERR_INVALID_ARGUMENT),
+    (dict(batch=0), ops.MLA_ERR_INVALID_ARGUMENT),
+    (dict(cap=100), ops.MLA_ERR_UNSUPPORTED),
+    (dict(num_pages=1 << 40), ops.MLA_ERR_UNSUPPORTED),
+    (dict(ws_bytes=2 * 128 * 656 - 1), ops.MLA_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_patch_fails_closed(kw, status):
+    assert patch_call(**kw) == status
+    assert ops.mla_last_error_message()
+
+
 def test_binding_refuses_host_tensors():
     import torch
 

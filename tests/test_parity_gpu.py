@@ -308,6 +308,95 @@ def test_fp8_indexed_ignores_ids_past_topk_length():
     assert ops.mla_read_device_errors() == 0
 
 
+# ----------------------------------------------------------------------------- early pack + current-token patch
+
+def _current_token_case(seed):
+    """A sparse workload, the ids of each request's "current" tokens (one
+    selected, one not selected, and a -1 entry), and replacement records for them."""
+    w = W.sparse_workload("patch", seed, 3, 64, 192, [192, 100, 0], context=2048, s_q=2)
+    other = W.sparse_workload("patch-new", seed + 1000, 1, 64, 64, [64], context=4096)
+    new_recs = other.kcache_rec.reshape(-1, 656)
+    ids = np.full((w.batch, 3), -1, np.int32)
+    sel_all = set(int(x) for x in w.indices.reshape(-1) if x >= 0)
+    for r in range(w.batch):
+        n = int(w.seqlens[r])
+        if n > 0:
+            ids[r, 0] = w.indices[r, 1, n // 2]              # selected by token 1 of the request
+        pool_ids = np.arange(r * 32 * 64, (r + 1) * 32 * 64)  # this request's pages
+        ids[r, 1] = int(next(i for i in pool_ids if int(i) not in sel_all))
+    new_pool = w.kcache_rec.copy()
+    flat = new_pool.reshape(-1, 656)
+    for j, i in enumerate(x for x in ids.reshape(-1) if x >= 0):
+        flat[i] = new_recs[j]
+    return w, ids, new_pool
+
+
+def _patched_run(w, ids, new_pool, side_stream):
+    dev = torch.device("cuda:0")
+    t = G.dev_tensors(w)
+    kc = t["kcache_rec"]  # the pool as the early pack sees it
+    ws = torch.empty((ops.mla_packed_kv_workspace_size(w.batch, w.s_q, w.topk_capacity),), dtype=torch.uint8,
+                     device=dev)
+    new_dev = torch.from_numpy(new_pool).to(dev)
+    ids_dev = torch.from_numpy(ids).to(dev)
+    torch.cuda.synchronize()
+    if side_stream:
+        # the pack runs on its own stream while the main stream writes the current
+        # tokens' records into the pool (the pack may see old or new bytes for
+        # them; the patch rewrites exactly those slots afterwards)
+        side = torch.cuda.Stream()
+        ev = torch.cuda.Event()
+        with torch.cuda.stream(side):
+            ops.mla_pack_selected_kv(kc, t["indices"], t["seqlens"], ws)
+            ev.record(side)
+        kc.copy_(new_dev)
+        torch.cuda.current_stream().wait_event(ev)
+    else:
+        ops.mla_pack_selected_kv(kc, t["indices"], t["seqlens"], ws)
+        kc.copy_(new_dev)  # the current step's records land in the pool
+    ops.mla_patch_packed_kv(kc, t["indices"], t["seqlens"], ids_dev, ws)
+    torch.cuda.synchronize()
+    return t, ws
+
+
+@pytest.mark.parametrize("side_stream", [False, True], ids=["same-stream", "side-stream"])
+def test_patch_after_early_pack(side_stream):
+    """Pack before the current tokens' records are written, write them, patch:
+    the workspace equals a fresh pack of the new pool byte for byte, and the
+    packed decode equals the by-index decode of the new pool bit for bit."""
+    G.say(f"early pack + patch ({'side' if side_stream else 'same'} stream)")
+    w, ids, new_pool = _current_token_case(170)
+    ops.mla_read_device_errors()
+    t, ws = _patched_run(w, ids, new_pool, side_stream)
+    ref_ws = O.pack_selected_kv(new_pool, w.indices, w.seqlens)
+    assert not np.array_equal(ref_ws, O.pack_selected_kv(w.kcache_rec, w.indices, w.seqlens))  # the patch matters
+    assert np.array_equal(ws.cpu().numpy(), ref_ws.reshape(-1))
+    plan = ops.DecodePlan(t["seqlens"], w.s_q, w.h_q, ops.KV_FP8_PACKED)
+    out_p, lse_p = ops.mla_decode(t["q"], ws, None, t["seqlens"], w.scale, False, plan=plan,
+                                  kv_format=ops.KV_FP8_PACKED, topk_capacity=w.topk_capacity)
+    out_i, lse_i = ops.mla_decode(t["q"], t["kcache_rec"], t["indices"], t["seqlens"], w.scale, False, plan=plan,
+                                  kv_format=ops.KV_FP8_INDEXED, topk_capacity=w.topk_capacity)
+    torch.cuda.synchronize()
+    assert torch.equal(out_p, out_i) and torch.equal(lse_p, lse_i)
+    G.compare("patched", out_p, lse_p, *O.mla_sparse_decode(w.q_bits, new_pool, w.indices, w.seqlens, w.scale))
+    assert ops.mla_read_device_errors() == 0
+
+
+def test_patch_out_of_pool_id_sets_flag():
+    G.say("device flag: patch id outside the pool")
+    w = W.sparse_workload("patchbad", 171, 1, 64, 64, [10], context=512)
+    limit = w.kcache_rec.shape[0] * 64
+    w.indices[0, 0, 4] = limit + 3  # selected, outside the pool (the pack zero-fills and flags it)
+    t = G.dev_tensors(w)
+    ops.mla_read_device_errors()
+    ws = ops.mla_pack_selected_kv(t["kcache_rec"], t["indices"], t["seqlens"])
+    ids = torch.tensor([[limit + 3]], dtype=torch.int32, device="cuda:0")
+    ops.mla_patch_packed_kv(t["kcache_rec"], t["indices"], t["seqlens"], ids, ws)
+    torch.cuda.synchronize()
+    assert ops.mla_read_device_errors() & 2
+    assert not ws.view(-1, 656)[4].any()  # the slot stays as the pack left it: zero
+
+
 # ----------------------------------------------------------------------------- device-side contract checks
 
 def test_out_of_range_page_sets_flag_without_fault():
