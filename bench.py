@@ -67,6 +67,8 @@ def main():
                     help="also run one plain 1 GiB device copy (scales the HBM byte counters)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of HIP-graph replays of the step")
+    ap.add_argument("--sparse", action="store_true",
+                    help="time the sparse FP8 paths instead (pack, patch, packed and by-index decode)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -81,6 +83,8 @@ def main():
     from mla_paged_kv_amd import ops
     from mla_paged_kv_amd import workloads as W
 
+    if args.sparse:
+        return sparse_main(args)
     dev = torch.device("cuda:0")
     t0 = time.time()
     w = W.config("h")
@@ -124,6 +128,7 @@ def main():
         from oracle import oracle as orc
         from tests import gpu_helpers as G
 
+        G.say = log  # parity lines go to stderr: stdout carries the one JSON line
         sel = list(np.linspace(0, b - 1, args.oracle_requests).astype(int))
         sub = G.sub_workload(w, sel)
         threads = orc.default_threads()
@@ -255,6 +260,87 @@ def main():
                    "36% of a measured 1747 GB/s copy) -- another machine and likely another head count",
     }
     print(json.dumps(result), flush=True)
+
+
+def sparse_main(args):
+    """Sparse FP8 decode step on two workloads, three ways, each captured as a HIP
+    graph: the decode that gathers by id; pack + packed decode (pack not
+    hidden); patch + packed decode (pack hidden in an earlier overlap window,
+    only the current-token patch on the critical path).  Every path is checked
+    against the oracle first.  Prints one JSON line."""
+    import numpy as np
+    import torch
+
+    from mla_paged_kv_amd import ops
+    from mla_paged_kv_amd import workloads as W
+    from oracle import oracle as orc
+    from tests import gpu_helpers as G
+
+    G.say = log  # parity lines go to stderr: stdout carries the one JSON line
+    dev = torch.device("cuda:0")
+    cases = [("c5", W.config("c5")),
+             ("b64-h128-topk2048", W.sparse_workload("b64-h128-topk2048", 65, 64, 128, 2048, [2048] * 64,
+                                                     context=8192))]
+    results = {}
+    for name, w in cases:
+        t = G.dev_tensors(w)
+        b, s_q, h_q, cap = w.batch, w.s_q, w.h_q, w.topk_capacity
+        sel_bytes = int(w.seqlens.sum()) * s_q * ops.REC_BYTES
+        ws = torch.empty((ops.mla_packed_kv_workspace_size(b, s_q, cap),), dtype=torch.uint8, device=dev)
+        ids = t["indices"][:, 0, :1].contiguous()  # one selected current token per request
+        out = torch.empty((b, s_q, h_q, 512), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((b, s_q, h_q), dtype=torch.float32, device=dev)
+        plans = {f: ops.DecodePlan(t["seqlens"], s_q, h_q, f) for f in (ops.KV_FP8_INDEXED, ops.KV_FP8_PACKED)}
+
+        def decode(fmt):
+            p = plans[fmt]
+            ops.mla_get_decode_metadata(t["seqlens"], b, s_q, h_q, 1, p.num_parts, p.sched_meta, p.num_splits)
+            kv, ix = (t["kcache_rec"], t["indices"]) if fmt == ops.KV_FP8_INDEXED else (ws, None)
+            ops.mla_decode_fwd(t["q"], kv, fmt, ix, t["seqlens"], w.scale, False, p.sched_meta, p.num_splits, out,
+                               lse, p.workspace, topk_capacity=cap)
+            ops.mla_combine(p.num_splits, p.workspace, b, s_q, h_q, p.num_parts, out, lse)
+
+        steps = {
+            "by_index": lambda: decode(ops.KV_FP8_INDEXED),
+            "pack_then_packed": lambda: (ops.mla_pack_selected_kv(t["kcache_rec"], t["indices"], t["seqlens"], ws),
+                                         decode(ops.KV_FP8_PACKED)),
+            "patch_then_packed": lambda: (ops.mla_patch_packed_kv(t["kcache_rec"], t["indices"], t["seqlens"], ids,
+                                                                  ws),
+                                          decode(ops.KV_FP8_PACKED)),
+        }
+        ref_o, ref_l = orc.mla_sparse_decode(w.q_bits, w.kcache_rec, w.indices, w.seqlens, w.scale,
+                                             nthreads=orc.default_threads())
+        ops.mla_pack_selected_kv(t["kcache_rec"], t["indices"], t["seqlens"], ws)
+        row = {"batch": b, "h_q": h_q, "s_q": s_q, "topk_capacity": cap, "selected_bytes": sel_bytes}
+        for key, fn in steps.items():
+            fn()
+            torch.cuda.synchronize()
+            G.compare(f"{name}-{key}", out, lse, ref_o, ref_l)  # raises on a mismatch
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            for _ in range(args.warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                g.replay()
+            torch.cuda.synchronize()
+            us = (time.perf_counter() - t0) * 1e6 / args.steps
+            G.compare(f"{name}-{key}-graph", out, lse, ref_o, ref_l)
+            row[key + "_us"] = round(us, 2)
+            row[key + "_selected_GBps"] = round(sel_bytes / (us * 1e-6) / 1e9, 1)
+        results[name] = row
+        log(f"{name}: {row}")
+    flags = ops.mla_read_device_errors()
+    if flags:
+        raise SystemExit(f"device error flags set: {flags}")
+    print(json.dumps({
+        "metric": "sparse FP8 MLA decode step time (metadata, [pack or patch], decode, combine)",
+        "unit": "us", "higher_is_better": False, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "dtype": "fp8 e4m3 records, bf16 MFMA", "data": "synthetic",
+        "launch": "one HIP graph per path", "workloads": results,
+    }), flush=True)
 
 
 if __name__ == "__main__":
