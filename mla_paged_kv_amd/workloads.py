@@ -62,6 +62,7 @@ class Workload:
     indices: Optional[np.ndarray] = None      # int32 [b, s_q, cap]
     topk_capacity: int = 0
     num_parts: Optional[int] = None           # forced split count (None = library's choice)
+    dtype: str = "bf16"                       # encoding of q_bits / kcache_bits: "bf16" or "fp16" (IEEE binary16)
 
     @property
     def num_pages(self) -> int:
@@ -93,26 +94,33 @@ class Workload:
         return out
 
 
-def _normal_bf16(rng: np.random.Generator, shape, std=1.0) -> np.ndarray:
-    x = rng.standard_normal(size=shape, dtype=np.float32)
-    if std != 1.0:
-        x *= np.float32(std)
+def _to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 -> 16-bit patterns, round to nearest even (bf16, or IEEE binary16 via numpy)."""
+    if dtype == "fp16":
+        return x.astype(np.float16).view(np.uint16)
     return f32_to_bf16_bits(x)
 
 
-def _paged_pool(rng, num_pages, std, chunk=256):
-    """bf16 pool [pages, 64, 1, 576] of N(0, std^2) values, drawn page-chunk by page-chunk."""
+def _normal_bf16(rng: np.random.Generator, shape, std=1.0, dtype="bf16") -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return _to_bits(x, dtype)
+
+
+def _paged_pool(rng, num_pages, std, chunk=256, dtype="bf16"):
+    """16-bit pool [pages, 64, 1, 576] of N(0, std^2) values, drawn page-chunk by page-chunk."""
     pool = np.empty((num_pages, PAGE, 1, D_QK), np.uint16)
     for p0 in range(0, num_pages, chunk):
         p1 = min(num_pages, p0 + chunk)
-        pool[p0:p1] = _normal_bf16(rng, (p1 - p0, PAGE, 1, D_QK), std)
+        pool[p0:p1] = _normal_bf16(rng, (p1 - p0, PAGE, 1, D_QK), std, dtype)
     return pool
 
 
-def _seal_pool(pool, block_table, seqlens):
+def _seal_pool(pool, block_table, seqlens, dtype="bf16"):
     """Write the sentinel into every cache slot that no request may read."""
     used = np.zeros(pool.shape[0], bool)
-    sent = f32_to_bf16_bits(np.array([SENTINEL, -SENTINEL], np.float32))
+    sent = _to_bits(np.array([SENTINEL, -SENTINEL], np.float32), dtype)
     pattern = np.resize(sent, D_QK)
     for r, n in enumerate(seqlens):
         n = int(n)
@@ -126,8 +134,9 @@ def _seal_pool(pool, block_table, seqlens):
 
 
 def dense_workload(name, seed, batch, s_q, h_q, seqlens, pool_pages, std=1.0, causal=False, scale=None,
-                   max_pages=None, num_parts=None, block_table_mode="shuffled") -> Workload:
-    """Dense bf16 paged workload.  Draw order: q, pool, page permutation."""
+                   max_pages=None, num_parts=None, block_table_mode="shuffled", dtype="bf16") -> Workload:
+    """Dense paged workload (bf16, or fp16 with dtype="fp16").  Draw order: q, pool,
+    page permutation."""
     rng = np.random.default_rng(seed)
     seqlens = np.asarray(seqlens, np.int32)
     assert seqlens.shape == (batch,)
@@ -135,8 +144,8 @@ def dense_workload(name, seed, batch, s_q, h_q, seqlens, pool_pages, std=1.0, ca
     if max_pages is None:
         max_pages = max(1, max(pages_needed) if pages_needed else 1)
     assert sum(pages_needed) <= pool_pages, "pool too small"
-    q = _normal_bf16(rng, (batch, s_q, h_q, D_QK), std)
-    pool = _paged_pool(rng, pool_pages, std)
+    q = _normal_bf16(rng, (batch, s_q, h_q, D_QK), std, dtype)
+    pool = _paged_pool(rng, pool_pages, std, dtype=dtype)
     perm = rng.permutation(pool_pages).astype(np.int32)
     bt = np.full((batch, max_pages), -1, np.int32)
     pos = 0
@@ -144,11 +153,11 @@ def dense_workload(name, seed, batch, s_q, h_q, seqlens, pool_pages, std=1.0, ca
         k = pages_needed[r]
         bt[r, :k] = perm[pos:pos + k]
         pos += k
-    _seal_pool(pool, bt, seqlens)
+    _seal_pool(pool, bt, seqlens, dtype)
     if scale is None:
         scale = 1.0 / math.sqrt(D_QK)
     return Workload(name=name, seed=seed, batch=batch, s_q=s_q, h_q=h_q, scale=float(scale), causal=causal,
-                    q_bits=q, seqlens=seqlens, kcache_bits=pool, block_table=bt, num_parts=num_parts)
+                    q_bits=q, seqlens=seqlens, kcache_bits=pool, block_table=bt, num_parts=num_parts, dtype=dtype)
 
 
 def _records(rng, n_tokens, chunk=4096):

@@ -35,6 +35,10 @@
  *   key 512 + e = bf16 RoPE e.  Keys are the records named by indices[r][i][k]
  *   (physical token id = page * 64 + slot) for k < topk_length[r]; no causal mask.
  *
+ *   fp16 variant (the dense page's Summary and Test plan verify BF16 and FP16
+ *   instantiations): q and the cache rows are IEEE binary16 bit patterns
+ *   instead of bf16; everything else is the same.
+ *
  *   Pack: workspace[row][t][s][0:656] = record(indices[row][t*64+s]) when
  *   t*64+s < topk_length, else 656 zero bytes (byte copy, no arithmetic).
  *
@@ -70,6 +74,20 @@ static double bf16_bits_to_f64(uint16_t b) {
   return (double)f;
 }
 
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits with bias 15, 10 fraction
+ * bits.  Exponent 0 encodes subnormals f * 2^-24; exponent 31 encodes
+ * infinities (f = 0) and NaNs. */
+double oracle_f16_to_f64(uint16_t b) {
+  int sign = (b >> 15) & 1;
+  int e = (b >> 10) & 0x1F;
+  int f = b & 0x3FF;
+  double v;
+  if (e == 0x1F) v = f ? NAN : INFINITY;
+  else if (e == 0) v = ldexp((double)f, -24);          /* (f / 1024) * 2^(1 - 15) */
+  else v = ldexp(1.0 + (double)f / 1024.0, e - 15);
+  return sign ? -v : v;
+}
+
 static double f32le_to_f64(const uint8_t* p) {
   uint32_t u = (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
   float f;
@@ -96,18 +114,23 @@ double oracle_e4m3fn_to_f64(uint8_t code) {
 /* ------------------------------------------------------------------ key sources */
 
 typedef struct {
-  int fp8;                   /* 0: bf16 rows of 576; 1: 656-byte FP8 records */
-  const uint16_t* kc_bf16;   /* [num_pages][64][576] */
+  int fp8;                   /* 0: 16-bit rows of 576; 1: 656-byte FP8 records */
+  const uint16_t* kc_bf16;   /* [num_pages][64][576], bf16 or (f16 set) binary16 */
   const uint8_t* kc_rec;     /* [num_pages][64][656] */
   int64_t num_pages;
+  int f16;                   /* 16-bit rows (and q) are binary16 */
 } kv_pool;
+
+static double half_bits_to_f64(const kv_pool* p, uint16_t b) {
+  return p->f16 ? oracle_f16_to_f64(b) : bf16_bits_to_f64(b);
+}
 
 /* Decode the key stored at physical token id `phys` into k[0:576]. */
 static int load_key(const kv_pool* p, int64_t phys, double* k) {
   if (phys < 0 || phys >= p->num_pages * PAGE) return OR_BAD_INDEX;
   if (!p->fp8) {
     const uint16_t* row = p->kc_bf16 + phys * D_QK;
-    for (int d = 0; d < D_QK; ++d) k[d] = bf16_bits_to_f64(row[d]);
+    for (int d = 0; d < D_QK; ++d) k[d] = half_bits_to_f64(p, row[d]);
   } else {
     const uint8_t* rec = p->kc_rec + phys * REC_BYTES;
     for (int d = 0; d < REC_NOPE; ++d) {
@@ -276,7 +299,7 @@ static int dense_row(const job* jb, int64_t row, int64_t* key_buf, double* score
   }
   double q[D_QK];
   const uint16_t* qr = c->q + row * D_QK;
-  for (int d = 0; d < D_QK; ++d) q[d] = bf16_bits_to_f64(qr[d]);
+  for (int d = 0; d < D_QK; ++d) q[d] = half_bits_to_f64(&c->pool, qr[d]);
   return attend(&c->pool, q, key_buf, j1 - j0, c->scale, score_buf, c->out + row * D_V, c->lse + row);
 }
 
@@ -288,7 +311,18 @@ int oracle_mla_decode(const uint16_t* q, const uint16_t* kcache, int64_t num_pag
                       double* out, double* lse, int nthreads) {
   if (!q || !kcache || !block_table || !seqlens || !out || !lse) return OR_BAD_ARG;
   if (batch < 0 || s_q < 1 || h_q < 1 || max_pages < 0 || num_pages < 0) return OR_BAD_ARG;
-  dense_ctx c = {{0, kcache, NULL, num_pages}, q, block_table, seqlens, batch, s_q, h_q, max_pages,
+  dense_ctx c = {{0, kcache, NULL, num_pages, 0}, q, block_table, seqlens, batch, s_q, h_q, max_pages,
+                 scale, causal, out, lse, NULL, NULL};
+  return run_rows(dense_row, &c, (int64_t)batch * s_q * h_q, (int64_t)max_pages * PAGE, nthreads);
+}
+
+/* Same, with q and kcache as IEEE binary16 bit patterns. */
+int oracle_mla_decode_f16(const uint16_t* q, const uint16_t* kcache, int64_t num_pages, const int32_t* block_table,
+                          int max_pages, const int32_t* seqlens, int batch, int s_q, int h_q, double scale,
+                          int causal, double* out, double* lse, int nthreads) {
+  if (!q || !kcache || !block_table || !seqlens || !out || !lse) return OR_BAD_ARG;
+  if (batch < 0 || s_q < 1 || h_q < 1 || max_pages < 0 || num_pages < 0) return OR_BAD_ARG;
+  dense_ctx c = {{0, kcache, NULL, num_pages, 1}, q, block_table, seqlens, batch, s_q, h_q, max_pages,
                  scale, causal, out, lse, NULL, NULL};
   return run_rows(dense_row, &c, (int64_t)batch * s_q * h_q, (int64_t)max_pages * PAGE, nthreads);
 }
@@ -302,7 +336,7 @@ int oracle_mla_decode_partial(const uint16_t* q, const uint16_t* kcache, int64_t
                               double* out, double* lse, int nthreads) {
   if (!q || !kcache || !block_table || !seqlens || !out || !lse || !split_lo || !split_hi) return OR_BAD_ARG;
   if (batch < 0 || s_q < 1 || h_q < 1 || max_pages < 0 || num_pages < 0) return OR_BAD_ARG;
-  dense_ctx c = {{0, kcache, NULL, num_pages}, q, block_table, seqlens, batch, s_q, h_q, max_pages,
+  dense_ctx c = {{0, kcache, NULL, num_pages, 0}, q, block_table, seqlens, batch, s_q, h_q, max_pages,
                  scale, causal, out, lse, split_lo, split_hi};
   return run_rows(dense_row, &c, (int64_t)batch * s_q * h_q, (int64_t)max_pages * PAGE, nthreads);
 }

@@ -69,6 +69,10 @@ def _load():
             lib.oracle_e4m3fn_to_f64.restype = f64
             lib.oracle_mla_decode.argtypes = [P, P, i64, P, i32, P, i32, i32, i32, f64, i32, P, P, i32]
             lib.oracle_mla_decode.restype = i32
+            lib.oracle_mla_decode_f16.argtypes = [P, P, i64, P, i32, P, i32, i32, i32, f64, i32, P, P, i32]
+            lib.oracle_mla_decode_f16.restype = i32
+            lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+            lib.oracle_f16_to_f64.restype = f64
             lib.oracle_mla_decode_partial.argtypes = [P, P, i64, P, i32, P, i32, i32, i32, f64, i32, P, P, P, P, i32]
             lib.oracle_mla_decode_partial.restype = i32
             lib.oracle_lse_combine.argtypes = [i32, P, P, P, P]
@@ -110,10 +114,17 @@ def e4m3fn_to_f64(code: int) -> float:
     return _load().oracle_e4m3fn_to_f64(int(code) & 0xFF)
 
 
-def mla_decode(q_bits, kcache_bits, block_table, seqlens, scale, causal, nthreads=None):
-    """Dense decode.  q_bits uint16 [b, s_q, h_q, 576] (bf16 bit patterns);
-    kcache_bits uint16 [pages, 64, 1, 576]; block_table int32 [b, max_pages];
-    seqlens int32 [b].  Returns (out fp64 [b, s_q, h_q, 512], lse fp64 [b, s_q, h_q])."""
+def f16_to_f64(code: int) -> float:
+    """IEEE binary16 bit pattern -> float (exact)."""
+    return _load().oracle_f16_to_f64(int(code) & 0xFFFF)
+
+
+def mla_decode(q_bits, kcache_bits, block_table, seqlens, scale, causal, nthreads=None, dtype="bf16"):
+    """Dense decode.  q_bits uint16 [b, s_q, h_q, 576] (bf16 bit patterns, or
+    IEEE binary16 ones with dtype="fp16"); kcache_bits uint16 [pages, 64, 1, 576]
+    (same encoding); block_table int32 [b, max_pages]; seqlens int32 [b].
+    Returns (out fp64 [b, s_q, h_q, 512], lse fp64 [b, s_q, h_q])."""
+    assert dtype in ("bf16", "fp16")
     q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
     kcache_bits = np.ascontiguousarray(kcache_bits, dtype=np.uint16)
     block_table = np.ascontiguousarray(block_table, dtype=np.int32)
@@ -123,7 +134,8 @@ def mla_decode(q_bits, kcache_bits, block_table, seqlens, scale, causal, nthread
     assert block_table.shape[0] == b and seqlens.shape == (b,)
     out = np.zeros((b, s_q, h_q, D_V), np.float64)
     lse = np.zeros((b, s_q, h_q), np.float64)
-    st = _load().oracle_mla_decode(
+    fn = _load().oracle_mla_decode if dtype == "bf16" else _load().oracle_mla_decode_f16
+    st = fn(
         _ptr(q_bits), _ptr(kcache_bits), kcache_bits.shape[0], _ptr(block_table), block_table.shape[1],
         _ptr(seqlens), b, s_q, h_q, float(scale), int(bool(causal)), _ptr(out), _ptr(lse),
         nthreads or default_threads())

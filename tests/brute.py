@@ -16,9 +16,15 @@ def bf16(bits):
     return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def dense(q_bits, kcache_bits, block_table, seqlens, scale, causal):
-    q = bf16(q_bits)                      # [b, s_q, h, 576]
-    kc = bf16(kcache_bits)[:, :, 0, :]    # [pages, 64, 576]
+def f16(bits):
+    """IEEE binary16 bit patterns -> float64 through numpy's float16."""
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+def dense(q_bits, kcache_bits, block_table, seqlens, scale, causal, dtype="bf16"):
+    dec = f16 if dtype == "fp16" else bf16
+    q = dec(q_bits)                       # [b, s_q, h, 576]
+    kc = dec(kcache_bits)[:, :, 0, :]     # [pages, 64, 576]
     b, s_q, h, _ = q.shape
     out = np.zeros((b, s_q, h, D_V))
     lse = np.full((b, s_q, h), -np.inf)

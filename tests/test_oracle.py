@@ -50,6 +50,37 @@ def test_dense_matches_brute_force(seed, b, s_q, h, seqlens, pool, causal):
     assert np.all(lse[~fin] == -np.inf) and np.all(out[~fin] == 0)
 
 
+@pytest.mark.parametrize("seed,b,s_q,h,seqlens,pool,causal", [
+    (21, 2, 1, 4, [1, 130], 5, False),
+    (22, 2, 3, 4, [65, 64], 4, True),
+    (23, 3, 2, 2, [0, 7, 200], 8, True),
+])
+def test_dense_fp16_matches_brute_force(seed, b, s_q, h, seqlens, pool, causal):
+    """The binary16 variant: same brute force with numpy's float16 decode."""
+    w = W.dense_workload("tiny16", seed, b, s_q, h, seqlens, pool_pages=pool, causal=causal, dtype="fp16")
+    out, lse = O.mla_decode(w.q_bits, w.kcache_bits, w.block_table, w.seqlens, w.scale, w.causal, nthreads=3,
+                            dtype="fp16")
+    bo, bl = brute.dense(w.q_bits, w.kcache_bits, w.block_table, w.seqlens, w.scale, causal, dtype="fp16")
+    np.testing.assert_allclose(out, bo, rtol=0, atol=1e-12)
+    fin = np.isfinite(bl)
+    assert np.array_equal(fin, np.isfinite(lse))
+    np.testing.assert_allclose(lse[fin], bl[fin], rtol=0, atol=1e-12)
+    # decoding the same bits as bf16 gives a different result (the encoding is really used)
+    ob, _ = O.mla_decode(w.q_bits, w.kcache_bits, w.block_table, w.seqlens, w.scale, w.causal, nthreads=3)
+    assert not np.allclose(ob, out)
+
+
+def test_f16_all_codes_match_numpy():
+    """IEEE 754 binary16: every one of the 65536 codes against numpy's float16."""
+    ref = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float64)
+    mine = np.array([O.f16_to_f64(c) for c in range(65536)])
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(mine)) and nan.sum() == 2 * 1023
+    assert np.array_equal(mine[~nan], ref[~nan])
+    assert O.f16_to_f64(0x3C00) == 1.0 and O.f16_to_f64(0x7BFF) == 65504.0 and O.f16_to_f64(0x0001) == 2.0 ** -24
+    assert O.f16_to_f64(0x7C00) == math.inf and O.f16_to_f64(0xFC00) == -math.inf
+
+
 def test_thread_count_does_not_change_result():
     w = tiny_dense(16, 2, 2, 4, [100, 190], 6, causal=True)
     a = run_oracle(w, nthreads=1)
