@@ -84,8 +84,11 @@ typedef enum {
 typedef enum {
   MLA_KV_BF16_PAGED = 0,  /* kcache bf16 pages reached through block_table */
   MLA_KV_FP8_PACKED = 1,  /* the workspace written by mla_pack_selected_kv */
-  MLA_KV_FP8_INDEXED = 2  /* the FP8 record pool itself, records gathered by
+  MLA_KV_FP8_INDEXED = 2, /* the FP8 record pool itself, records gathered by
                              top-k index inside the decode (no pack) */
+  MLA_KV_FP16_PAGED = 3   /* as MLA_KV_BF16_PAGED with q, kcache and out in
+                             IEEE fp16 (binary16) -- the FP16 instantiation the
+                             dense page's Test plan lists */
 } mla_kv_format;
 
 /* Text of the last error on the calling host thread ("" if none).  The
@@ -138,8 +141,11 @@ int mla_get_decode_metadata(const int32_t* seqlens, int batch, int s_q, int h_q,
  * online softmax and writes either the final out/lse rows (request not split)
  * or a split partial into `workspace`.  mla_combine must follow on the same
  * stream to finish split requests.
- *   q (device) bf16 [batch][s_q][h_q][576]
+ *   q (device) bf16 [batch][s_q][h_q][576] (fp16 for MLA_KV_FP16_PAGED)
  *   kv (device): MLA_KV_BF16_PAGED -> kcache bf16 [num_pages][64][1][576];
+ *                MLA_KV_FP16_PAGED -> kcache fp16 [num_pages][64][1][576], the
+ *                same paging, masks and scope as bf16; P is rounded to fp16
+ *                before PV and out is fp16;
  *                MLA_KV_FP8_PACKED -> packed workspace of mla_pack_selected_kv
  *                (then block_table/max_pages/num_pages are ignored, seqlens is
  *                topk_length, h_q must be 64 or 128, no causal; query token s of
@@ -162,7 +168,8 @@ int mla_get_decode_metadata(const int32_t* seqlens, int batch, int s_q, int h_q,
  *                  MLA_ERR_INVALID_ARGUMENT; causal: 0/1
  *   sched_meta, num_splits (device): from mla_get_decode_metadata with the same
  *     seqlens, batch and num_parts
- *   out (device) bf16 [batch][s_q][h_q][512], lse (device) fp32 [batch][s_q][h_q]
+ *   out (device) bf16 [batch][s_q][h_q][512] (fp16 for MLA_KV_FP16_PAGED), lse
+ *     (device) fp32 [batch][s_q][h_q]
  *   workspace (device) of >= mla_decode_workspace_size(batch, s_q, h_q, num_parts)
  * Scope: h_kv = 1; h_q a multiple of 16 with h_q <= 128; s_q * h_q <= 2048;
  * gfx950 device. */
@@ -176,9 +183,11 @@ int mla_decode_fwd(const void* q, const void* kv, int kv_format, int64_t num_pag
  * out = sum_i exp(lse_i - L) * o_i, lse = L (a split with lse -inf has weight
  * 0); a request with 0 splits (no key) gets out = 0, lse = -inf; a request with
  * one split was finished by mla_decode_fwd and is left untouched.  The split
- * count is a runtime value; there is no fixed ladder of supported counts. */
+ * count is a runtime value; there is no fixed ladder of supported counts.
+ * kv_format is the one the decode ran with: out is fp16 for
+ * MLA_KV_FP16_PAGED, bf16 otherwise; the partials are fp32 either way. */
 int mla_combine(const int32_t* num_splits, const void* workspace, size_t workspace_bytes, int batch, int s_q,
-                int h_q, int num_parts, void* out, float* lse, void* stream);
+                int h_q, int num_parts, int kv_format, void* out, float* lse, void* stream);
 
 /* Pack (device): copies the selected 656-byte records byte-for-byte into the
  * tile-major workspace ws[row][tile][slot][656], row = r * s_q + i,

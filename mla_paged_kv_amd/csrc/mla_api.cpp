@@ -76,9 +76,10 @@ int check_shape(int batch, int s_q, int h_q, int h_kv, int kv_format) {
   if (h_kv != 1) return fail(MLA_ERR_UNSUPPORTED, "h_kv %d: only one latent KV head is supported", h_kv);
   if (h_q % 16 != 0 || h_q > 128) return fail(MLA_ERR_UNSUPPORTED, "h_q %d: must be a multiple of 16 and <= 128", h_q);
   if ((int64_t)s_q * h_q > MLA_MAX_ROWS) return fail(MLA_ERR_UNSUPPORTED, "s_q * h_q = %d above %d", s_q * h_q, MLA_MAX_ROWS);
-  if (kv_format != MLA_KV_BF16_PAGED && kv_format != MLA_KV_FP8_PACKED && kv_format != MLA_KV_FP8_INDEXED)
+  if (kv_format != MLA_KV_BF16_PAGED && kv_format != MLA_KV_FP8_PACKED && kv_format != MLA_KV_FP8_INDEXED &&
+      kv_format != MLA_KV_FP16_PAGED)
     return fail(MLA_ERR_UNSUPPORTED, "kv_format %d unknown", kv_format);
-  if (kv_format != MLA_KV_BF16_PAGED) {
+  if (kv_format == MLA_KV_FP8_PACKED || kv_format == MLA_KV_FP8_INDEXED) {
     if (h_q != 64 && h_q != 128) return fail(MLA_ERR_UNSUPPORTED, "sparse FP8 decode supports h_q in {64, 128} (got %d)", h_q);
   }
   return MLA_OK;
@@ -159,7 +160,7 @@ int mla_decode_fwd(const void* q, const void* kv, int kv_format, int64_t num_pag
     return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
   int st = check_shape(batch, s_q, h_q, h_kv, kv_format);
   if (st) return st;
-  const bool fp8 = kv_format != MLA_KV_BF16_PAGED;
+  const bool fp8 = kv_format == MLA_KV_FP8_PACKED || kv_format == MLA_KV_FP8_INDEXED;
   if (fp8) {
     if (topk_capacity < mla::kPage || topk_capacity % mla::kPage != 0)
       return fail(MLA_ERR_UNSUPPORTED, "topk_capacity %d must be a positive multiple of 64", topk_capacity);
@@ -210,6 +211,7 @@ int mla_decode_fwd(const void* q, const void* kv, int kv_format, int64_t num_pag
   a.part_lse = a.part_o + (size_t)a.slots * a.M * mla::kDV;
   const int kind = kv_format == MLA_KV_FP8_PACKED    ? mla::kDecodeFp8Packed
                    : kv_format == MLA_KV_FP8_INDEXED ? mla::kDecodeFp8Indexed
+                   : kv_format == MLA_KV_FP16_PAGED  ? mla::kDecodeF16
                                                      : mla::kDecodeBf16;
   hipError_t e = mla::launch_decode(a, kind, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
@@ -217,9 +219,9 @@ int mla_decode_fwd(const void* q, const void* kv, int kv_format, int64_t num_pag
 }
 
 int mla_combine(const int32_t* num_splits, const void* workspace, size_t workspace_bytes, int batch, int s_q,
-                int h_q, int num_parts, void* out, float* lse, void* stream) {
+                int h_q, int num_parts, int kv_format, void* out, float* lse, void* stream) {
   if (!num_splits || !workspace || !out || !lse) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
-  int st = check_shape(batch, s_q, h_q, 1, MLA_KV_BF16_PAGED);
+  int st = check_shape(batch, s_q, h_q, 1, kv_format);
   if (st) return st;
   if (num_parts < 1 || num_parts > MLA_MAX_PARTS)
     return fail(MLA_ERR_INVALID_ARGUMENT, "num_parts %d out of [1, %d]", num_parts, MLA_MAX_PARTS);
@@ -231,7 +233,7 @@ int mla_combine(const int32_t* num_splits, const void* workspace, size_t workspa
   const float* part_o = (const float*)workspace;
   const float* part_lse = part_o + (size_t)slots_for(batch, num_parts) * M * mla::kDV;
   hipError_t e = mla::launch_combine(num_splits, part_o, part_lse, batch, M, slots_for(batch, num_parts),
-                                     (uint16_t*)out, lse, (hipStream_t)stream);
+                                     kv_format == MLA_KV_FP16_PAGED, (uint16_t*)out, lse, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   return ok();
 }

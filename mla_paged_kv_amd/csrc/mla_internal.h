@@ -23,7 +23,7 @@ constexpr int kErrSeqlen = 4;
 constexpr int kErrMeta = 8;
 
 struct DecodeArgs {
-  const uint16_t* q;          // bf16 bits [batch][s_q][h_q][576]
+  const uint16_t* q;          // bf16 (fp16 for kDecodeF16) bits [batch][s_q][h_q][576]
   const uint8_t* kv;          // bf16 pages, packed FP8 records, or the FP8 record pool
   int64_t num_pages;
   const int32_t* block_table; // [batch][max_pages]; FP8 indexed: top-k token ids [batch][s_q][cap]
@@ -36,7 +36,7 @@ struct DecodeArgs {
   const int32_t* sched_meta;  // [num_parts][8]
   const int32_t* num_splits;  // [batch + 1]
   int num_parts;
-  uint16_t* out;              // bf16 bits [batch][M][512]
+  uint16_t* out;              // bf16 (fp16 for kDecodeF16) bits [batch][M][512]
   float* lse;                 // [batch][M]
   float* part_o;              // [slots][M][512]
   float* part_lse;            // [slots][M]
@@ -48,11 +48,12 @@ int decode_row_blocks_per_wg(int M);
 
 hipError_t launch_sched(const int32_t* lengths, int batch, int num_parts, int32_t* meta, int32_t* num_splits,
                         hipStream_t stream);
-// Decode kernel family: bf16 pages, FP8 packed workspace, FP8 pool gathered by index.
-enum DecodeKind { kDecodeBf16 = 0, kDecodeFp8Packed = 1, kDecodeFp8Indexed = 2 };
+// Decode kernel family: bf16 pages, FP8 packed workspace, FP8 pool gathered by
+// index, fp16 pages.
+enum DecodeKind { kDecodeBf16 = 0, kDecodeFp8Packed = 1, kDecodeFp8Indexed = 2, kDecodeF16 = 3 };
 hipError_t launch_decode(const DecodeArgs& a, int kind, hipStream_t stream);
 hipError_t launch_combine(const int32_t* num_splits, const float* part_o, const float* part_lse, int batch, int M,
-                          int slots, uint16_t* out, float* lse, hipStream_t stream);
+                          int slots, bool out_f16, uint16_t* out, float* lse, hipStream_t stream);
 hipError_t launch_pack(const uint8_t* kcache, int64_t num_pages, const int32_t* indices, const int32_t* topk_length,
                        int batch, int s_q, int cap, uint8_t* ws, hipStream_t stream);
 hipError_t launch_patch(const uint8_t* kcache, int64_t num_pages, const int32_t* indices, const int32_t* topk_length,

@@ -499,6 +499,28 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
 }
 
+// Element type of the dense path: bf16 or IEEE binary16 (fp16).  Tiles,
+// fragments and transposed reads move 16-bit patterns either way; only the
+// MFMA and the conversions of P and of the output differ.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+template <bool F16>
+__device__ __forceinline__ f32x4 mfma16t(bf16x8 a, bf16x8 b, f32x4 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                  0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// two floats -> two 16-bit values (round to nearest even), a in the low half
+template <bool F16>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (F16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), f16x2));
+  else
+    return pack_bf16x2(a, b);
+}
+
 // One workgroup: the 16*RB query rows of row block blockIdx.y, over the KV range
 // of partition blockIdx.x.  Wave w computes scores for rows [16w, 16w+16) (if
 // w < RB) and accumulates output columns [128w, 128w+128) for all rows.
@@ -805,7 +827,7 @@ struct NoHook {
   __device__ void operator()(int) const {}
 };
 
-template <int D, class Hook = NoHook>
+template <int D, bool F16 = false, class Hook = NoHook>
 __device__ __forceinline__ void qk_tile(const LDS_AS uint8_t* kt, uint32_t base0, uint32_t base1,
                                         const bf16x8 (&qreg)[18], f32x4 (&acc)[2], const Hook& hook = Hook()) {
   static_assert(D >= 2 && D <= 8, "K operand ring depth");
@@ -826,8 +848,8 @@ __device__ __forceinline__ void qk_tile(const LDS_AS uint8_t* kt, uint32_t base0
       k0[(s + D - 1) % D] = lds_read_b128(kt + addr(s + D - 1));
       k1[(s + D - 1) % D] = lds_read_b128(kt + addr(s + D - 1) + 16 * kRowBytes);
     }
-    c[0][s & 1] = mfma16(k0[s % D], qreg[s], c[0][s & 1]);
-    c[1][s & 1] = mfma16(k1[s % D], qreg[s], c[1][s & 1]);
+    c[0][s & 1] = mfma16t<F16>(k0[s % D], qreg[s], c[0][s & 1]);
+    c[1][s & 1] = mfma16t<F16>(k1[s % D], qreg[s], c[1][s & 1]);
     hook(s);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -868,7 +890,7 @@ __device__ __forceinline__ void zero_tail_rows_256(LDS_AS uint8_t* kt, int nvali
   }
 }
 
-template <int RB>
+template <int RB, bool F16>
 __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) {
   constexpr int MB = 16 * RB;
   __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[kDLdsBytes];
@@ -1040,10 +1062,10 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
             s67 = pv[6] + pv[7];
             break;
           case 15:
-            wp[0] = pack_bf16x2(pv[0], pv[1]);
-            wp[1] = pack_bf16x2(pv[2], pv[3]);
-            wp[2] = pack_bf16x2(pv[4], pv[5]);
-            wp[3] = pack_bf16x2(pv[6], pv[7]);
+            wp[0] = pack2<F16>(pv[0], pv[1]);
+            wp[1] = pack2<F16>(pv[2], pv[3]);
+            wp[2] = pack2<F16>(pv[4], pv[5]);
+            wp[3] = pack2<F16>(pv[6], pv[7]);
             s01 += s23;
             s45 += s67;
             break;
@@ -1093,11 +1115,11 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
             if constexpr (DO_SM) {
               const f32x4 prev[2] = {sacc[0], sacc[1]};
               // one softmax step after each k-step
-              qk_tile<kQkDepth>(kt, kq_base0, kq_base1, qreg, acc, [&](int s) {
+              qk_tile<kQkDepth, F16>(kt, kq_base0, kq_base1, qreg, acc, [&](int s) {
                 softmax_step(s, t - 1, prev);
               });
             } else {
-              qk_tile<kQkDepth>(kt, kq_base0, kq_base1, qreg, acc);
+              qk_tile<kQkDepth, F16>(kt, kq_base0, kq_base1, qreg, acc);
             }
             sacc[0] = acc[0];
             sacc[1] = acc[1];
@@ -1196,7 +1218,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
           for (int db = 0; db < 8; ++db) {
             const bf16x8 av = __builtin_shufflevector(v[db][0], v[db][1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) o[db][rb] = mfma16(av, bp[rb], o[db][rb]);
+            for (int rb = 0; rb < RB; ++rb) o[db][rb] = mfma16t<F16>(av, bp[rb], o[db][rb]);
             if constexpr (DO_VREAD) vread(tv, db);
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -1231,7 +1253,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
 #pragma unroll
           for (int db = 0; db < 8; ++db) {
             const f32x4 vv = o[db][rb] * inv;
-            *reinterpret_cast<u32x2*>(orow + 16 * db) = u32x2{pack_bf16x2(vv[0], vv[1]), pack_bf16x2(vv[2], vv[3])};
+            *reinterpret_cast<u32x2*>(orow + 16 * db) = u32x2{pack2<F16>(vv[0], vv[1]), pack2<F16>(vv[2], vv[3])};
           }
         } else {
           float* prow = a.part_o + ((int64_t)slot * a.M + rho_o) * kDV + 128 * w + 4 * g;
@@ -1267,8 +1289,10 @@ static hipError_t launch_decode_t(const DecodeArgs& a, int kind, hipStream_t str
     hipLaunchKernelGGL((decode_kernel<RB, true, false>), grid, dim3(kDecodeThreads), 0, stream, a);
   else if (kind == kDecodeFp8Indexed)
     hipLaunchKernelGGL((decode_kernel<RB, true, true>), grid, dim3(kDecodeThreads), 0, stream, a);
+  else if (kind == kDecodeF16)
+    hipLaunchKernelGGL((decode_ws_kernel<RB, true>), grid, dim3(kWsThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_ws_kernel<RB>), grid, dim3(kWsThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_ws_kernel<RB, false>), grid, dim3(kWsThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -1286,7 +1310,9 @@ static hipError_t occupancy_t(int kind, int* n) {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_kernel<RB, true, false>, kDecodeThreads, 0);
   if (kind == kDecodeFp8Indexed)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_kernel<RB, true, true>, kDecodeThreads, 0);
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_ws_kernel<RB>, kWsThreads, 0);
+  if (kind == kDecodeF16)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_ws_kernel<RB, true>, kWsThreads, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_ws_kernel<RB, false>, kWsThreads, 0);
 }
 
 hipError_t decode_occupancy(int kind, int M, int* wgs_per_cu) {
@@ -1303,6 +1329,7 @@ hipError_t decode_occupancy(int kind, int M, int* wgs_per_cu) {
 
 // ------------------------------------------------------------------ combine
 // One wave per (request, row); lane l owns output columns [8l, 8l+8).
+template <bool F16>
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ num_splits,
                                                       const float* __restrict__ part_o,
                                                       const float* __restrict__ part_lse, int M, int slots,
@@ -1337,10 +1364,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
     acc1 += wgt * *reinterpret_cast<const f32x4*>(src + 4);
   }
   u32x4 pk;
-  pk.x = (uint32_t)f32_to_bf16_rne(acc0[0]) | ((uint32_t)f32_to_bf16_rne(acc0[1]) << 16);
-  pk.y = (uint32_t)f32_to_bf16_rne(acc0[2]) | ((uint32_t)f32_to_bf16_rne(acc0[3]) << 16);
-  pk.z = (uint32_t)f32_to_bf16_rne(acc1[0]) | ((uint32_t)f32_to_bf16_rne(acc1[1]) << 16);
-  pk.w = (uint32_t)f32_to_bf16_rne(acc1[2]) | ((uint32_t)f32_to_bf16_rne(acc1[3]) << 16);
+  pk.x = pack2<F16>(acc0[0], acc0[1]);
+  pk.y = pack2<F16>(acc0[2], acc0[3]);
+  pk.z = pack2<F16>(acc1[0], acc1[1]);
+  pk.w = pack2<F16>(acc1[2], acc1[3]);
   *reinterpret_cast<u32x4*>(orow) = pk;
   if (l == 0) lse[(int64_t)r * M + rho] = L;
 }
@@ -1428,9 +1455,14 @@ hipError_t launch_sched(const int32_t* lengths, int batch, int num_parts, int32_
 }
 
 hipError_t launch_combine(const int32_t* num_splits, const float* part_o, const float* part_lse, int batch, int M,
-                          int slots, uint16_t* out, float* lse, hipStream_t stream) {
+                          int slots, bool out_f16, uint16_t* out, float* lse, hipStream_t stream) {
   dim3 grid(batch, (M + 3) / 4);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, stream, num_splits, part_o, part_lse, M, slots, out, lse);
+  if (out_f16)
+    hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, stream, num_splits, part_o, part_lse, M, slots, out,
+                       lse);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, stream, num_splits, part_o, part_lse, M, slots, out,
+                       lse);
   return hipGetLastError();
 }
 

@@ -34,6 +34,7 @@ MLA_ERR_HIP = -4
 KV_BF16_PAGED = 0
 KV_FP8_PACKED = 1
 KV_FP8_INDEXED = 2
+KV_FP16_PAGED = 3
 D_QK, D_V, PAGE, REC_BYTES = 576, 512, 64, 656
 SCHED_META_INTS = 8
 
@@ -49,7 +50,7 @@ _SIGS = {
     "mla_get_decode_metadata": ([_P, _i32, _i32, _i32, _i32, _i32, _P, _P, _P], _i32),
     "mla_decode_fwd": ([_P, _P, _i32, _i64, _P, _i32, _P, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _P, _P, _i32,
                         _P, _P, _P, _sz, _P], _i32),
-    "mla_combine": ([_P, _P, _sz, _i32, _i32, _i32, _i32, _P, _P, _P], _i32),
+    "mla_combine": ([_P, _P, _sz, _i32, _i32, _i32, _i32, _i32, _P, _P, _P], _i32),
     "mla_pack_selected_kv": ([_P, _i64, _P, _P, _i32, _i32, _i32, _P, _sz, _P], _i32),
     "mla_patch_packed_kv": ([_P, _i64, _P, _P, _i32, _i32, _i32, _P, _i32, _P, _sz, _P], _i32),
     "mla_sparse_kv_format": ([_i32, _i32, _i32, _sz, _i32, _P], _i32),
@@ -138,14 +139,18 @@ def mla_get_decode_metadata(seqlens, batch, s_q, h_q, h_kv, num_parts, sched_met
     return sched_meta, num_splits
 
 
+def _act_dtype(kv_format):
+    return torch.float16 if kv_format == KV_FP16_PAGED else torch.bfloat16
+
+
 def mla_decode_fwd(q, kv, kv_format, block_table, seqlens, softmax_scale, causal, sched_meta, num_splits, out, lse,
                    workspace, topk_capacity=0, stream=None):
-    _need(q, "q", torch.bfloat16)
+    _need(q, "q", _act_dtype(kv_format))
     b, s_q, h_q, d = q.shape
     if d != D_QK:
         raise ValueError(f"q last dim {d}, expected {D_QK}")
-    if kv_format == KV_BF16_PAGED:
-        _need(kv, "kcache", torch.bfloat16)
+    if kv_format in (KV_BF16_PAGED, KV_FP16_PAGED):
+        _need(kv, "kcache", _act_dtype(kv_format))
         if tuple(kv.shape[1:]) != (PAGE, 1, D_QK):
             raise ValueError(f"kcache shape {tuple(kv.shape)}, expected [pages, 64, 1, 576]")
         _need(block_table, "block_table", torch.int32)
@@ -171,7 +176,7 @@ def mla_decode_fwd(q, kv, kv_format, block_table, seqlens, softmax_scale, causal
     _need(seqlens, "seqlens", torch.int32, (b,))
     _need(sched_meta, "sched_meta", torch.int32)
     _need(num_splits, "num_splits", torch.int32, (b + 1,))
-    _need(out, "out", torch.bfloat16, (b, s_q, h_q, D_V))
+    _need(out, "out", _act_dtype(kv_format), (b, s_q, h_q, D_V))
     _need(lse, "lse", torch.float32, (b, s_q, h_q))
     _need(workspace, "workspace", torch.uint8)
     _check(_lib.mla_decode_fwd(
@@ -181,13 +186,13 @@ def mla_decode_fwd(q, kv, kv_format, block_table, seqlens, softmax_scale, causal
         workspace.numel(), _stream(stream)))
 
 
-def mla_combine(num_splits, workspace, batch, s_q, h_q, num_parts, out, lse, stream=None):
+def mla_combine(num_splits, workspace, batch, s_q, h_q, num_parts, out, lse, stream=None, kv_format=KV_BF16_PAGED):
     _need(num_splits, "num_splits", torch.int32, (batch + 1,))
     _need(workspace, "workspace", torch.uint8)
-    _need(out, "out", torch.bfloat16, (batch, s_q, h_q, D_V))
+    _need(out, "out", _act_dtype(kv_format), (batch, s_q, h_q, D_V))
     _need(lse, "lse", torch.float32, (batch, s_q, h_q))
     _check(_lib.mla_combine(_ptr(num_splits), _ptr(workspace), workspace.numel(), batch, s_q, h_q, num_parts,
-                            _ptr(out), _ptr(lse), _stream(stream)))
+                            kv_format, _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def mla_pack_selected_kv(kcache_fp8, indices, topk_length, workspace=None, stream=None):
@@ -265,10 +270,11 @@ def mla_decode(q, kv, block_table, seqlens, softmax_scale=None, causal=False, pl
     if plan is None:
         plan = DecodePlan(seqlens, s_q, h_q, kv_format, stream=stream)
     if out is None:
-        out = torch.empty((b, s_q, h_q, D_V), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((b, s_q, h_q, D_V), dtype=_act_dtype(kv_format), device=q.device)
     if lse is None:
         lse = torch.empty((b, s_q, h_q), dtype=torch.float32, device=q.device)
     mla_decode_fwd(q, kv, kv_format, block_table, seqlens, softmax_scale, causal, plan.sched_meta, plan.num_splits,
                    out, lse, plan.workspace, topk_capacity=topk_capacity, stream=stream)
-    mla_combine(plan.num_splits, plan.workspace, b, s_q, h_q, plan.num_parts, out, lse, stream=stream)
+    mla_combine(plan.num_splits, plan.workspace, b, s_q, h_q, plan.num_parts, out, lse, stream=stream,
+                kv_format=kv_format)
     return out, lse

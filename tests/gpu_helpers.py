@@ -21,13 +21,14 @@ def say(msg):
 
 def dev_tensors(w, device="cuda:0"):
     t = {}
-    t["q"] = torch.from_numpy(w.q_bits.view(np.int16)).to(device).view(torch.bfloat16)
+    act = torch.float16 if getattr(w, "dtype", "bf16") == "fp16" else torch.bfloat16
+    t["q"] = torch.from_numpy(w.q_bits.view(np.int16)).to(device).view(act)
     t["seqlens"] = torch.from_numpy(w.seqlens).to(device)
     if w.fp8:
         t["kcache_rec"] = torch.from_numpy(w.kcache_rec).to(device)
         t["indices"] = torch.from_numpy(w.indices).to(device)
     else:
-        t["kcache"] = torch.from_numpy(w.kcache_bits.view(np.int16)).to(device).view(torch.bfloat16)
+        t["kcache"] = torch.from_numpy(w.kcache_bits.view(np.int16)).to(device).view(act)
         t["block_table"] = torch.from_numpy(w.block_table).to(device)
     return t
 
@@ -35,8 +36,10 @@ def dev_tensors(w, device="cuda:0"):
 def run_dense(w, t=None, num_parts=None):
     t = t or dev_tensors(w)
     parts = num_parts if num_parts is not None else w.num_parts
-    plan = ops.DecodePlan(t["seqlens"], w.s_q, w.h_q, ops.KV_BF16_PAGED, num_parts=parts)
-    out, lse = ops.mla_decode(t["q"], t["kcache"], t["block_table"], t["seqlens"], w.scale, w.causal, plan=plan)
+    fmt = ops.KV_FP16_PAGED if getattr(w, "dtype", "bf16") == "fp16" else ops.KV_BF16_PAGED
+    plan = ops.DecodePlan(t["seqlens"], w.s_q, w.h_q, fmt, num_parts=parts)
+    out, lse = ops.mla_decode(t["q"], t["kcache"], t["block_table"], t["seqlens"], w.scale, w.causal, plan=plan,
+                              kv_format=fmt)
     torch.cuda.synchronize()
     return out, lse, plan
 

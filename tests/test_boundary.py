@@ -82,6 +82,9 @@ def decode_call(**kw):
     (dict(h_q=144), ops.MLA_ERR_UNSUPPORTED),
     (dict(s_q=17, h_q=128), ops.MLA_ERR_UNSUPPORTED),     # 2176 rows > 2048
     (dict(fmt=7), ops.MLA_ERR_UNSUPPORTED),
+    (dict(fmt=ops.KV_FP16_PAGED, h_kv=2), ops.MLA_ERR_UNSUPPORTED),
+    (dict(fmt=ops.KV_FP16_PAGED, h_q=136), ops.MLA_ERR_UNSUPPORTED),
+    (dict(fmt=ops.KV_FP16_PAGED, bt=NULL), ops.MLA_ERR_INVALID_ARGUMENT),
     (dict(fmt=ops.KV_FP8_PACKED, cap=2048, h_q=96), ops.MLA_ERR_UNSUPPORTED),
     (dict(fmt=ops.KV_FP8_PACKED, cap=2000, h_q=64), ops.MLA_ERR_UNSUPPORTED),
     (dict(fmt=ops.KV_FP8_PACKED, cap=2048, h_q=128, s_q=17), ops.MLA_ERR_UNSUPPORTED),
@@ -120,8 +123,9 @@ def test_metadata_and_combine_and_pack_fail_closed():
     assert lib.mla_get_decode_metadata(NULL, 2, 1, 128, 1, 8, FAKE, FAKE, NULL) == ops.MLA_ERR_INVALID_ARGUMENT
     assert lib.mla_get_decode_metadata(FAKE, 2, 1, 128, 1, 0, FAKE, FAKE, NULL) == ops.MLA_ERR_INVALID_ARGUMENT
     assert lib.mla_get_decode_metadata(FAKE, 2, 1, 128, 3, 8, FAKE, FAKE, NULL) == ops.MLA_ERR_UNSUPPORTED
-    assert lib.mla_combine(FAKE, FAKE, 10, 2, 1, 128, 8, FAKE, FAKE, NULL) == ops.MLA_ERR_WORKSPACE_TOO_SMALL
-    assert lib.mla_combine(NULL, FAKE, 1 << 40, 2, 1, 128, 8, FAKE, FAKE, NULL) == ops.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_combine(FAKE, FAKE, 10, 2, 1, 128, 8, 0, FAKE, FAKE, NULL) == ops.MLA_ERR_WORKSPACE_TOO_SMALL
+    assert lib.mla_combine(NULL, FAKE, 1 << 40, 2, 1, 128, 8, 0, FAKE, FAKE, NULL) == ops.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_combine(FAKE, FAKE, 1 << 40, 2, 1, 128, 8, 9, FAKE, FAKE, NULL) == ops.MLA_ERR_UNSUPPORTED
     assert lib.mla_pack_selected_kv(FAKE, 16, FAKE, FAKE, 2, 1, 100, FAKE, 1 << 40, NULL) == ops.MLA_ERR_UNSUPPORTED
     assert lib.mla_pack_selected_kv(FAKE, 16, FAKE, FAKE, 2, 1, 128, FAKE, 10, NULL) == ops.MLA_ERR_WORKSPACE_TOO_SMALL
     assert lib.mla_pack_selected_kv(FAKE, 0, FAKE, FAKE, 2, 1, 128, FAKE, 1 << 40, NULL) == ops.MLA_ERR_INVALID_ARGUMENT

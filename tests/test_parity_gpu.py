@@ -20,7 +20,7 @@ ops = pytest.importorskip("mla_paged_kv_amd.ops")
 
 
 def oracle_dense(w):
-    return O.mla_decode(w.q_bits, w.kcache_bits, w.block_table, w.seqlens, w.scale, w.causal)
+    return O.mla_decode(w.q_bits, w.kcache_bits, w.block_table, w.seqlens, w.scale, w.causal, dtype=w.dtype)
 
 
 def oracle_sparse(w):
@@ -79,6 +79,28 @@ def test_dense_small(case):
     out, lse, plan = G.run_dense(w)
     ref = oracle_dense(w)
     G.compare(name, out, lse, *ref)
+
+
+DENSE_FP16 = [
+    # name, seed, b, s_q, h_q, seqlens, pool pages, causal, forced parts, std
+    ("fp16-ragged-h128", 120, 3, 1, 128, [1, 700, 2049], 60, False, None, 1.0),
+    ("fp16-ragged-h128-p7", 121, 3, 1, 128, [64, 1000, 333], 40, False, 7, 1.0),
+    ("fp16-h16", 122, 2, 1, 16, [333, 64], 8, False, None, 1.0),
+    ("fp16-h48-p3", 123, 2, 1, 48, [31, 500], 10, False, 3, 1.0),
+    ("fp16-causal-sq4-h64", 124, 2, 4, 64, [3, 300], 8, True, None, 1.0),
+    ("fp16-large-values", 125, 2, 1, 128, [500, 129], 12, False, None, 8.0),  # scores far from 0, |x| up to ~40
+]
+
+
+@pytest.mark.parametrize("case", DENSE_FP16, ids=[c[0] for c in DENSE_FP16])
+def test_dense_fp16(case):
+    name, seed, b, s_q, h_q, seqlens, pool, causal, parts, std = case
+    G.say(f"dense fp16 {name}")
+    w = W.dense_workload(name, seed, b, s_q, h_q, seqlens, pool_pages=pool, causal=causal, num_parts=parts, std=std,
+                         dtype="fp16")
+    out, lse, plan = G.run_dense(w)
+    assert out.dtype == torch.float16
+    G.compare(name, out, lse, *oracle_dense(w))
 
 
 @pytest.mark.parametrize("cfg", ["c1", "c2"])
