@@ -56,7 +56,7 @@ class Workload:
     q_bits: np.ndarray                      # uint16 [b, s_q, h_q, 576]
     seqlens: np.ndarray                     # int32 [b] (sparse: topk_length)
     fp8: bool = False
-    kcache_bits: Optional[np.ndarray] = None  # uint16 [pages, 64, 1, 576]
+    kcache_bits: Optional[np.ndarray] = None  # uint16 [pages, 64, h_kv, 576]
     block_table: Optional[np.ndarray] = None  # int32 [b, max_pages]
     kcache_rec: Optional[np.ndarray] = None   # uint8 [pages, 64, 1, 656]
     indices: Optional[np.ndarray] = None      # int32 [b, s_q, cap]
@@ -108,12 +108,12 @@ def _normal_bf16(rng: np.random.Generator, shape, std=1.0, dtype="bf16") -> np.n
     return _to_bits(x, dtype)
 
 
-def _paged_pool(rng, num_pages, std, chunk=256, dtype="bf16"):
-    """16-bit pool [pages, 64, 1, 576] of N(0, std^2) values, drawn page-chunk by page-chunk."""
-    pool = np.empty((num_pages, PAGE, 1, D_QK), np.uint16)
+def _paged_pool(rng, num_pages, std, chunk=256, dtype="bf16", h_kv=1):
+    """16-bit pool [pages, 64, h_kv, 576] of N(0, std^2) values, drawn page-chunk by page-chunk."""
+    pool = np.empty((num_pages, PAGE, h_kv, D_QK), np.uint16)
     for p0 in range(0, num_pages, chunk):
         p1 = min(num_pages, p0 + chunk)
-        pool[p0:p1] = _normal_bf16(rng, (p1 - p0, PAGE, 1, D_QK), std, dtype)
+        pool[p0:p1] = _normal_bf16(rng, (p1 - p0, PAGE, h_kv, D_QK), std, dtype)
     return pool
 
 
@@ -129,14 +129,14 @@ def _seal_pool(pool, block_table, seqlens, dtype="bf16"):
             pg = block_table[r, k]
             used[pg] = True
             if k == npg - 1 and n % PAGE:
-                pool[pg, n % PAGE:, 0, :] = pattern
+                pool[pg, n % PAGE:, :, :] = pattern
     pool[~used] = pattern
 
 
 def dense_workload(name, seed, batch, s_q, h_q, seqlens, pool_pages, std=1.0, causal=False, scale=None,
-                   max_pages=None, num_parts=None, block_table_mode="shuffled", dtype="bf16") -> Workload:
-    """Dense paged workload (bf16, or fp16 with dtype="fp16").  Draw order: q, pool,
-    page permutation."""
+                   max_pages=None, num_parts=None, block_table_mode="shuffled", dtype="bf16", h_kv=1) -> Workload:
+    """Dense paged workload (bf16, or fp16 with dtype="fp16"; h_kv KV heads per
+    token).  Draw order: q, pool, page permutation."""
     rng = np.random.default_rng(seed)
     seqlens = np.asarray(seqlens, np.int32)
     assert seqlens.shape == (batch,)
@@ -145,7 +145,7 @@ def dense_workload(name, seed, batch, s_q, h_q, seqlens, pool_pages, std=1.0, ca
         max_pages = max(1, max(pages_needed) if pages_needed else 1)
     assert sum(pages_needed) <= pool_pages, "pool too small"
     q = _normal_bf16(rng, (batch, s_q, h_q, D_QK), std, dtype)
-    pool = _paged_pool(rng, pool_pages, std, dtype=dtype)
+    pool = _paged_pool(rng, pool_pages, std, dtype=dtype, h_kv=h_kv)
     perm = rng.permutation(pool_pages).astype(np.int32)
     bt = np.full((batch, max_pages), -1, np.int32)
     pos = 0

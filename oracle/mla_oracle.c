@@ -35,6 +35,10 @@
  *   key 512 + e = bf16 RoPE e.  Keys are the records named by indices[r][i][k]
  *   (physical token id = page * 64 + slot) for k < topk_length[r]; no causal mask.
  *
+ *   Several KV heads (the dense page's Test plan sweeps hk = 1..4): the cache
+ *   is [pages][64][h_kv][576] and query head h reads KV head h / (h_q / h_kv),
+ *   the query heads being grouped contiguously.
+ *
  *   fp16 variant (the dense page's Summary and Test plan verify BF16 and FP16
  *   instantiations): q and the cache rows are IEEE binary16 bit patterns
  *   instead of bf16; everything else is the same.
@@ -119,15 +123,18 @@ typedef struct {
   const uint8_t* kc_rec;     /* [num_pages][64][656] */
   int64_t num_pages;
   int f16;                   /* 16-bit rows (and q) are binary16 */
+  int h_kv;                  /* 16-bit rows per token (KV heads); 0 is read as 1 */
 } kv_pool;
 
 static double half_bits_to_f64(const kv_pool* p, uint16_t b) {
   return p->f16 ? oracle_f16_to_f64(b) : bf16_bits_to_f64(b);
 }
 
-/* Decode the key stored at physical token id `phys` into k[0:576]. */
+/* Decode key `phys` into k[0:576]: a physical token id, or for 16-bit rows
+ * with h_kv > 1 the row (token id * h_kv + KV head). */
 static int load_key(const kv_pool* p, int64_t phys, double* k) {
-  if (phys < 0 || phys >= p->num_pages * PAGE) return OR_BAD_INDEX;
+  const int64_t rows_per_token = (!p->fp8 && p->h_kv > 1) ? p->h_kv : 1;
+  if (phys < 0 || phys >= p->num_pages * PAGE * rows_per_token) return OR_BAD_INDEX;
   if (!p->fp8) {
     const uint16_t* row = p->kc_bf16 + phys * D_QK;
     for (int d = 0; d < D_QK; ++d) k[d] = half_bits_to_f64(p, row[d]);
@@ -292,10 +299,12 @@ static int dense_row(const job* jb, int64_t row, int64_t* key_buf, double* score
     if (j1 > n) j1 = n;
     if (j1 < j0) j1 = j0;
   }
+  const int h_kv = c->pool.h_kv > 1 ? c->pool.h_kv : 1;
+  const int kvh = h / (c->h_q / h_kv);  /* KV head of query head h */
   for (int64_t j = j0; j < j1; ++j) {
     int64_t page = c->block_table[(int64_t)r * c->max_pages + j / PAGE];
     if (page < 0 || page >= c->pool.num_pages) return OR_BAD_PAGE;
-    key_buf[j - j0] = page * PAGE + j % PAGE;
+    key_buf[j - j0] = (page * PAGE + j % PAGE) * h_kv + kvh;
   }
   double q[D_QK];
   const uint16_t* qr = c->q + row * D_QK;
@@ -311,7 +320,7 @@ int oracle_mla_decode(const uint16_t* q, const uint16_t* kcache, int64_t num_pag
                       double* out, double* lse, int nthreads) {
   if (!q || !kcache || !block_table || !seqlens || !out || !lse) return OR_BAD_ARG;
   if (batch < 0 || s_q < 1 || h_q < 1 || max_pages < 0 || num_pages < 0) return OR_BAD_ARG;
-  dense_ctx c = {{0, kcache, NULL, num_pages, 0}, q, block_table, seqlens, batch, s_q, h_q, max_pages,
+  dense_ctx c = {{0, kcache, NULL, num_pages, 0, 1}, q, block_table, seqlens, batch, s_q, h_q, max_pages,
                  scale, causal, out, lse, NULL, NULL};
   return run_rows(dense_row, &c, (int64_t)batch * s_q * h_q, (int64_t)max_pages * PAGE, nthreads);
 }
@@ -322,8 +331,21 @@ int oracle_mla_decode_f16(const uint16_t* q, const uint16_t* kcache, int64_t num
                           int causal, double* out, double* lse, int nthreads) {
   if (!q || !kcache || !block_table || !seqlens || !out || !lse) return OR_BAD_ARG;
   if (batch < 0 || s_q < 1 || h_q < 1 || max_pages < 0 || num_pages < 0) return OR_BAD_ARG;
-  dense_ctx c = {{0, kcache, NULL, num_pages, 1}, q, block_table, seqlens, batch, s_q, h_q, max_pages,
+  dense_ctx c = {{0, kcache, NULL, num_pages, 1, 1}, q, block_table, seqlens, batch, s_q, h_q, max_pages,
                  scale, causal, out, lse, NULL, NULL};
+  return run_rows(dense_row, &c, (int64_t)batch * s_q * h_q, (int64_t)max_pages * PAGE, nthreads);
+}
+
+/* Dense decode with h_kv KV heads: kcache [num_pages][64][h_kv][576] (bf16, or
+ * binary16 if f16), query head h reads KV head h / (h_q / h_kv); h_kv divides h_q. */
+int oracle_mla_decode_hkv(const uint16_t* q, const uint16_t* kcache, int64_t num_pages, const int32_t* block_table,
+                          int max_pages, const int32_t* seqlens, int batch, int s_q, int h_q, int h_kv, int f16,
+                          double scale, int causal, double* out, double* lse, int nthreads) {
+  if (!q || !kcache || !block_table || !seqlens || !out || !lse) return OR_BAD_ARG;
+  if (batch < 0 || s_q < 1 || h_q < 1 || max_pages < 0 || num_pages < 0) return OR_BAD_ARG;
+  if (h_kv < 1 || h_q % h_kv != 0) return OR_BAD_ARG;
+  dense_ctx c = {{0, kcache, NULL, num_pages, f16 ? 1 : 0, h_kv}, q, block_table, seqlens, batch, s_q, h_q,
+                 max_pages, scale, causal, out, lse, NULL, NULL};
   return run_rows(dense_row, &c, (int64_t)batch * s_q * h_q, (int64_t)max_pages * PAGE, nthreads);
 }
 
@@ -336,7 +358,7 @@ int oracle_mla_decode_partial(const uint16_t* q, const uint16_t* kcache, int64_t
                               double* out, double* lse, int nthreads) {
   if (!q || !kcache || !block_table || !seqlens || !out || !lse || !split_lo || !split_hi) return OR_BAD_ARG;
   if (batch < 0 || s_q < 1 || h_q < 1 || max_pages < 0 || num_pages < 0) return OR_BAD_ARG;
-  dense_ctx c = {{0, kcache, NULL, num_pages, 0}, q, block_table, seqlens, batch, s_q, h_q, max_pages,
+  dense_ctx c = {{0, kcache, NULL, num_pages, 0, 1}, q, block_table, seqlens, batch, s_q, h_q, max_pages,
                  scale, causal, out, lse, split_lo, split_hi};
   return run_rows(dense_row, &c, (int64_t)batch * s_q * h_q, (int64_t)max_pages * PAGE, nthreads);
 }

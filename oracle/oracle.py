@@ -71,6 +71,8 @@ def _load():
             lib.oracle_mla_decode.restype = i32
             lib.oracle_mla_decode_f16.argtypes = [P, P, i64, P, i32, P, i32, i32, i32, f64, i32, P, P, i32]
             lib.oracle_mla_decode_f16.restype = i32
+            lib.oracle_mla_decode_hkv.argtypes = [P, P, i64, P, i32, P, i32, i32, i32, i32, i32, f64, i32, P, P, i32]
+            lib.oracle_mla_decode_hkv.restype = i32
             lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
             lib.oracle_f16_to_f64.restype = f64
             lib.oracle_mla_decode_partial.argtypes = [P, P, i64, P, i32, P, i32, i32, i32, f64, i32, P, P, P, P, i32]
@@ -121,10 +123,27 @@ def f16_to_f64(code: int) -> float:
 
 def mla_decode(q_bits, kcache_bits, block_table, seqlens, scale, causal, nthreads=None, dtype="bf16"):
     """Dense decode.  q_bits uint16 [b, s_q, h_q, 576] (bf16 bit patterns, or
-    IEEE binary16 ones with dtype="fp16"); kcache_bits uint16 [pages, 64, 1, 576]
-    (same encoding); block_table int32 [b, max_pages]; seqlens int32 [b].
+    IEEE binary16 ones with dtype="fp16"); kcache_bits uint16 [pages, 64, h_kv, 576]
+    (same encoding; query head h reads KV head h // (h_q // h_kv)); block_table
+    int32 [b, max_pages]; seqlens int32 [b].
     Returns (out fp64 [b, s_q, h_q, 512], lse fp64 [b, s_q, h_q])."""
     assert dtype in ("bf16", "fp16")
+    h_kv = kcache_bits.shape[2]
+    if h_kv != 1:
+        q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+        kcache_bits = np.ascontiguousarray(kcache_bits, dtype=np.uint16)
+        block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+        seqlens = np.ascontiguousarray(seqlens, dtype=np.int32)
+        b, s_q, h_q, _ = q_bits.shape
+        assert kcache_bits.shape[1] == PAGE and kcache_bits.shape[3] == D_QK and h_q % h_kv == 0
+        out = np.zeros((b, s_q, h_q, D_V), np.float64)
+        lse = np.zeros((b, s_q, h_q), np.float64)
+        st = _load().oracle_mla_decode_hkv(
+            _ptr(q_bits), _ptr(kcache_bits), kcache_bits.shape[0], _ptr(block_table), block_table.shape[1],
+            _ptr(seqlens), b, s_q, h_q, h_kv, int(dtype == "fp16"), float(scale), int(bool(causal)), _ptr(out),
+            _ptr(lse), nthreads or default_threads())
+        _check(st, "mla_decode")
+        return out, lse
     q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
     kcache_bits = np.ascontiguousarray(kcache_bits, dtype=np.uint16)
     block_table = np.ascontiguousarray(block_table, dtype=np.int32)

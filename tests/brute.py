@@ -24,8 +24,10 @@ def f16(bits):
 def dense(q_bits, kcache_bits, block_table, seqlens, scale, causal, dtype="bf16"):
     dec = f16 if dtype == "fp16" else bf16
     q = dec(q_bits)                       # [b, s_q, h, 576]
-    kc = dec(kcache_bits)[:, :, 0, :]     # [pages, 64, 576]
+    kc_all = dec(kcache_bits)             # [pages, 64, h_kv, 576]
+    h_kv = kc_all.shape[2]
     b, s_q, h, _ = q.shape
+    g = h // h_kv                         # query heads per KV head
     out = np.zeros((b, s_q, h, D_V))
     lse = np.full((b, s_q, h), -np.inf)
     for r in range(b):
@@ -33,9 +35,11 @@ def dense(q_bits, kcache_bits, block_table, seqlens, scale, causal, dtype="bf16"
         if n == 0:
             continue
         j = np.arange(n)
-        K = kc[block_table[r, j // PAGE], j % PAGE]          # [n, 576]
-        S = scale * (q[r].reshape(s_q * h, D_QK) @ K.T)      # [s_q*h, n]
-        S = S.reshape(s_q, h, n)
+        Kall = kc_all[block_table[r, j // PAGE], j % PAGE]   # [n, h_kv, 576]
+        S = np.empty((s_q, h, n))
+        for kk in range(h_kv):                                # heads of group kk use KV head kk
+            Qg = q[r][:, kk * g:(kk + 1) * g].reshape(s_q * g, D_QK)
+            S[:, kk * g:(kk + 1) * g] = scale * (Qg @ Kall[:, kk].T).reshape(s_q, g, n)
         mask = np.ones((s_q, n), bool)
         if causal:
             for i in range(s_q):
@@ -44,7 +48,8 @@ def dense(q_bits, kcache_bits, block_table, seqlens, scale, causal, dtype="bf16"
         L = logsumexp(S, axis=2)                              # [s_q, h]
         ok = np.isfinite(L)
         P = np.where(ok[:, :, None], np.exp(S - np.where(ok, L, 0)[:, :, None]), 0.0)
-        out[r] = P @ K[:, :D_V]
+        for kk in range(h_kv):
+            out[r][:, kk * g:(kk + 1) * g] = P[:, kk * g:(kk + 1) * g] @ Kall[:, kk, :D_V]
         lse[r] = L
     return out, lse
 

@@ -70,6 +70,32 @@ def test_dense_fp16_matches_brute_force(seed, b, s_q, h, seqlens, pool, causal):
     assert not np.allclose(ob, out)
 
 
+@pytest.mark.parametrize("seed,b,s_q,h,h_kv,seqlens,pool,causal,dtype", [
+    (31, 2, 1, 4, 2, [1, 130], 5, False, "bf16"),
+    (32, 2, 2, 8, 4, [65, 90], 4, True, "bf16"),
+    (33, 1, 3, 6, 3, [200], 4, True, "fp16"),
+])
+def test_dense_multi_kv_head_matches_brute_force(seed, b, s_q, h, h_kv, seqlens, pool, causal, dtype):
+    w = W.dense_workload("tinyhk", seed, b, s_q, h, seqlens, pool_pages=pool, causal=causal, dtype=dtype, h_kv=h_kv)
+    assert w.kcache_bits.shape[2] == h_kv
+    out, lse = O.mla_decode(w.q_bits, w.kcache_bits, w.block_table, w.seqlens, w.scale, w.causal, nthreads=3,
+                            dtype=dtype)
+    bo, bl = brute.dense(w.q_bits, w.kcache_bits, w.block_table, w.seqlens, w.scale, causal, dtype=dtype)
+    np.testing.assert_allclose(out, bo, rtol=0, atol=1e-12)
+    fin = np.isfinite(bl)
+    np.testing.assert_allclose(lse[fin], bl[fin], rtol=0, atol=1e-12)
+
+
+def test_multi_kv_head_groups_read_their_own_head():
+    """Each group of h_q / h_kv query heads equals an h_kv = 1 decode over that KV head alone."""
+    w = W.dense_workload("hkgroups", 34, 2, 2, 8, [70, 150], pool_pages=5, causal=True, h_kv=4)
+    out, lse = O.mla_decode(w.q_bits, w.kcache_bits, w.block_table, w.seqlens, w.scale, w.causal, nthreads=3)
+    for kk in range(4):
+        o1, l1 = O.mla_decode(w.q_bits[:, :, 2 * kk:2 * kk + 2], w.kcache_bits[:, :, kk:kk + 1], w.block_table,
+                              w.seqlens, w.scale, w.causal, nthreads=3)
+        assert np.array_equal(o1, out[:, :, 2 * kk:2 * kk + 2]) and np.array_equal(l1, lse[:, :, 2 * kk:2 * kk + 2])
+
+
 def test_f16_all_codes_match_numpy():
     """IEEE 754 binary16: every one of the 65536 codes against numpy's float16."""
     ref = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float64)
