@@ -38,7 +38,11 @@
  *
  * Layouts (all row-major, contiguous):
  *   q            bf16  [batch][s_q][h_q][576]
- *   kcache       bf16  [num_pages][64][1][576]           (MLA_KV_BF16_PAGED)
+ *   kcache       bf16  [num_pages][64][h_kv][576]        (MLA_KV_BF16_PAGED; fp16
+ *                  for MLA_KV_FP16_PAGED).  Query head h reads KV head
+ *                  h / (h_q / h_kv): the h_q heads form h_kv contiguous groups
+ *                  (multi-KV-head decode, swept over hk = 1..4 in the dense
+ *                  page's Test plan); MLA itself has h_kv = 1.
  *   kcache_fp8   uint8 [num_pages][64][1][656]           656-byte records:
  *                  bytes [0,512) E4M3FN NoPE, [512,528) 4 x fp32 LE scales
  *                  (scale k covers NoPE dims [128k, 128k+128)), [528,656)
@@ -72,6 +76,7 @@ extern "C" {
 #define MLA_MAX_ROWS 2048      /* s_q * h_q per request */
 #define MLA_MAX_BATCH 65536
 #define MLA_MAX_PARTS 8192
+#define MLA_MAX_KV_HEADS 16    /* h_kv (dense formats; the sparse FP8 formats have 1) */
 
 typedef enum {
   MLA_OK = 0,
@@ -108,7 +113,8 @@ int mla_decode_num_parts(int batch, int s_q, int h_q, int h_kv, int kv_format, i
 /* The same policy as a pure function of the device figures (for tests and for
  * callers planning for another device): cus = compute units, wgs_per_cu =
  * decode workgroups resident per CU. */
-int mla_plan_num_parts(int batch, int s_q, int h_q, int kv_format, int cus, int wgs_per_cu, int* num_parts_out);
+int mla_plan_num_parts(int batch, int s_q, int h_q, int h_kv, int kv_format, int cus, int wgs_per_cu,
+                       int* num_parts_out);
 
 /* Bytes of the caller-owned decode workspace (split partials: fp32 partial
  * outputs and lse for at most batch + num_parts splits).  0 on bad input. */
@@ -136,14 +142,15 @@ size_t mla_packed_kv_workspace_size(int batch, int s_q, int topk_capacity);
 int mla_get_decode_metadata(const int32_t* seqlens, int batch, int s_q, int h_q, int h_kv, int num_parts,
                             int32_t* sched_meta, int32_t* num_splits, void* stream);
 
-/* Decode (device).  Launches num_parts x ceil(s_q*h_q / R) workgroups (R = 16,
- * 32 or 64 query rows per workgroup); each walks its partition's pages with an
+/* Decode (device).  Launches num_parts x h_kv * ceil(s_q*h_q/h_kv / R) workgroups
+ * (R = 16, 32 or 64 query rows of one KV head per workgroup); each walks its
+ * partition's pages with an
  * online softmax and writes either the final out/lse rows (request not split)
  * or a split partial into `workspace`.  mla_combine must follow on the same
  * stream to finish split requests.
  *   q (device) bf16 [batch][s_q][h_q][576] (fp16 for MLA_KV_FP16_PAGED)
- *   kv (device): MLA_KV_BF16_PAGED -> kcache bf16 [num_pages][64][1][576];
- *                MLA_KV_FP16_PAGED -> kcache fp16 [num_pages][64][1][576], the
+ *   kv (device): MLA_KV_BF16_PAGED -> kcache bf16 [num_pages][64][h_kv][576];
+ *                MLA_KV_FP16_PAGED -> kcache fp16 [num_pages][64][h_kv][576], the
  *                same paging, masks and scope as bf16; P is rounded to fp16
  *                before PV and out is fp16;
  *                MLA_KV_FP8_PACKED -> packed workspace of mla_pack_selected_kv
@@ -171,8 +178,8 @@ int mla_get_decode_metadata(const int32_t* seqlens, int batch, int s_q, int h_q,
  *   out (device) bf16 [batch][s_q][h_q][512] (fp16 for MLA_KV_FP16_PAGED), lse
  *     (device) fp32 [batch][s_q][h_q]
  *   workspace (device) of >= mla_decode_workspace_size(batch, s_q, h_q, num_parts)
- * Scope: h_kv = 1; h_q a multiple of 16 with h_q <= 128; s_q * h_q <= 2048;
- * gfx950 device. */
+ * Scope: h_q a multiple of 16 with h_q <= 128; 1 <= h_kv <= 16 dividing h_q
+ * (the FP8 formats: h_kv = 1); s_q * h_q <= 2048; gfx950 device. */
 int mla_decode_fwd(const void* q, const void* kv, int kv_format, int64_t num_pages, const int32_t* block_table,
                    int max_pages, const int32_t* seqlens, int topk_capacity, int batch, int s_q, int h_q, int h_kv,
                    float softmax_scale, int causal, const int32_t* sched_meta, const int32_t* num_splits,

@@ -73,13 +73,15 @@ int check_shape(int batch, int s_q, int h_q, int h_kv, int kv_format) {
     return fail(MLA_ERR_UNSUPPORTED, "batch %d above the scheduler limit %d", batch, mla::kSchedMaxBatch);
   if (s_q < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "s_q %d < 1", s_q);
   if (h_q < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "h_q %d < 1", h_q);
-  if (h_kv != 1) return fail(MLA_ERR_UNSUPPORTED, "h_kv %d: only one latent KV head is supported", h_kv);
+  if (h_kv < 1 || h_kv > MLA_MAX_KV_HEADS || h_q % h_kv != 0)
+    return fail(MLA_ERR_UNSUPPORTED, "h_kv %d: must divide h_q and be in [1, %d]", h_kv, MLA_MAX_KV_HEADS);
   if (h_q % 16 != 0 || h_q > 128) return fail(MLA_ERR_UNSUPPORTED, "h_q %d: must be a multiple of 16 and <= 128", h_q);
   if ((int64_t)s_q * h_q > MLA_MAX_ROWS) return fail(MLA_ERR_UNSUPPORTED, "s_q * h_q = %d above %d", s_q * h_q, MLA_MAX_ROWS);
   if (kv_format != MLA_KV_BF16_PAGED && kv_format != MLA_KV_FP8_PACKED && kv_format != MLA_KV_FP8_INDEXED &&
       kv_format != MLA_KV_FP16_PAGED)
     return fail(MLA_ERR_UNSUPPORTED, "kv_format %d unknown", kv_format);
   if (kv_format == MLA_KV_FP8_PACKED || kv_format == MLA_KV_FP8_INDEXED) {
+    if (h_kv != 1) return fail(MLA_ERR_UNSUPPORTED, "sparse FP8 decode has one KV head (got h_kv %d)", h_kv);
     if (h_q != 64 && h_q != 128) return fail(MLA_ERR_UNSUPPORTED, "sparse FP8 decode supports h_q in {64, 128} (got %d)", h_q);
   }
   return MLA_OK;
@@ -93,14 +95,15 @@ extern "C" {
 
 const char* mla_last_error_message(void) { return g_last_error.c_str(); }
 
-int mla_plan_num_parts(int batch, int s_q, int h_q, int kv_format, int cus, int wgs_per_cu, int* num_parts_out) {
+int mla_plan_num_parts(int batch, int s_q, int h_q, int h_kv, int kv_format, int cus, int wgs_per_cu,
+                       int* num_parts_out) {
   if (!num_parts_out) return fail(MLA_ERR_INVALID_ARGUMENT, "num_parts_out is NULL");
-  int st = check_shape(batch, s_q, h_q, 1, kv_format);
+  int st = check_shape(batch, s_q, h_q, h_kv, kv_format);
   if (st) return st;
   if (cus < 1 || wgs_per_cu < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "cus %d / wgs_per_cu %d must be >= 1", cus, wgs_per_cu);
-  const int M = s_q * h_q;
-  const int rb = 16 * mla::decode_row_blocks_per_wg(M);
-  const int row_blocks = (M + rb - 1) / rb;
+  const int Mkv = s_q * (h_q / h_kv);  // rows per (request, KV head)
+  const int rb = 16 * mla::decode_row_blocks_per_wg(Mkv);
+  const int row_blocks = h_kv * ((Mkv + rb - 1) / rb);
   int64_t slots = (int64_t)cus * wgs_per_cu;
   int64_t parts = slots / row_blocks;
   if (parts < 1) parts = 1;
@@ -121,10 +124,10 @@ int mla_decode_num_parts(int batch, int s_q, int h_q, int h_kv, int kv_format, i
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail(e, "device query");
-  e = mla::decode_occupancy(kv_format, s_q * h_q, &wgs);
+  e = mla::decode_occupancy(kv_format, s_q * (h_q / h_kv), &wgs);
   if (e != hipSuccess) return hip_fail(e, "occupancy query");
   if (wgs < 1) return fail(MLA_ERR_HIP, "decode kernel does not fit on a CU");
-  return mla_plan_num_parts(batch, s_q, h_q, kv_format, cus, wgs, num_parts_out);
+  return mla_plan_num_parts(batch, s_q, h_q, h_kv, kv_format, cus, wgs, num_parts_out);
 }
 
 size_t mla_decode_workspace_size(int batch, int s_q, int h_q, int num_parts) {
@@ -199,6 +202,9 @@ int mla_decode_fwd(const void* q, const void* kv, int kv_format, int64_t num_pag
   a.s_q = s_q;
   a.h_q = h_q;
   a.M = s_q * h_q;
+  a.h_kv = h_kv;
+  a.G = h_q / h_kv;
+  a.Mkv = s_q * a.G;
   a.scale_log2 = softmax_scale * 1.44269504088896340736f;
   a.causal = causal ? 1 : 0;
   a.sched_meta = sched_meta;

@@ -24,13 +24,14 @@ constexpr int kErrMeta = 8;
 
 struct DecodeArgs {
   const uint16_t* q;          // bf16 (fp16 for kDecodeF16) bits [batch][s_q][h_q][576]
-  const uint8_t* kv;          // bf16 pages, packed FP8 records, or the FP8 record pool
+  const uint8_t* kv;          // 16-bit pages [pages][64][h_kv][576], packed FP8 records, or the FP8 record pool
   int64_t num_pages;
   const int32_t* block_table; // [batch][max_pages]; FP8 indexed: top-k token ids [batch][s_q][cap]
   int max_pages;
   const int32_t* seqlens;     // [batch] (packed: topk_length)
   int cap;                    // packed: top-k capacity (multiple of 64)
   int batch, s_q, h_q, M;     // M = s_q * h_q rows per request
+  int h_kv, G, Mkv;           // KV heads, query heads per KV head (h_q / h_kv), s_q * G
   float scale_log2;           // softmax_scale * log2(e)
   int causal;
   const int32_t* sched_meta;  // [num_parts][8]

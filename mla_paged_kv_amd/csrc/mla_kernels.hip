@@ -395,6 +395,41 @@ struct TileLoader<false> {
     const uint32_t voff = l56 + 16u * ((bits >> (3 * k)) & 7u);
     load_lds16_s(src + (uint64_t)(qi * 1024), voff, smem + kOffKDense + st * kTileBytes + qi * 1024);
   }
+
+  // Several KV heads per token: the cache is [pages][64][h_kv][576], so the key
+  // rows of one head are h_kv * 1152 bytes apart.  A lane's chunk of load k lies
+  // in key row (64 qi + l) / 72 (kept 5 bits per load); its source offset is the
+  // contiguous one plus row * (h_kv - 1) * 1152.
+  uint64_t rowbits;
+  __device__ void init_rows(int w, int l) {
+    rowbits = 0;
+#pragma unroll
+    for (int k = 0; k < kLoadsPerWave; ++k) {
+      const int qi = w + 4 * k;
+      rowbits |= (uint64_t)((qi * 64 + l) / kChunksPerRow) << (5 * k);
+    }
+  }
+  __device__ uint64_t tile_src_hkv(const DecodeArgs& a, int64_t page, int key0, int kvh) const {
+    if (page < 0 || page >= a.num_pages) {
+      if ((threadIdx.x & 63) == 0) atomicOr(&g_error_flags, kErrPage);
+      page = 0;
+    }
+    const uint64_t token = (uint64_t)page * kPage + (uint64_t)(key0 & 63);
+    const uint64_t off = (token * (uint64_t)a.h_kv + (uint64_t)kvh) * (uint64_t)kRowBytes;
+    return uniform_u64((uint64_t)(uintptr_t)a.kv + off);
+  }
+  __device__ void issue_page_hkv(const DecodeArgs& a, int64_t page, int key0, int kvh, LDS_AS uint8_t* smem, int st,
+                                 int w) const {
+    const uint64_t src = tile_src_hkv(a, page, key0, kvh);
+    const uint32_t xstride = (uint32_t)(a.h_kv - 1) * (uint32_t)kRowBytes;
+#pragma unroll
+    for (int k = 0; k < kLoadsPerWave; ++k) {
+      const int qi = w + 4 * k;
+      const uint32_t row = (uint32_t)(rowbits >> (5 * k)) & 31u;
+      const uint32_t voff = l56 + 16u * ((bits >> (3 * k)) & 7u) + row * xstride;
+      load_lds16_s(src + (uint64_t)(qi * 1024), voff, smem + kOffKDense + st * kTileBytes + qi * 1024);
+    }
+  }
 };
 
 // FP8 packed workspace: tile = 32 consecutive 656-byte records of one query row.
@@ -890,7 +925,7 @@ __device__ __forceinline__ void zero_tail_rows_256(LDS_AS uint8_t* kt, int nvali
   }
 }
 
-template <int RB, bool F16>
+template <int RB, bool F16, bool MKV>
 __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) {
   constexpr int MB = 16 * RB;
   __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[kDLdsBytes];
@@ -907,7 +942,19 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
   const int w = wv & 3;  // index within the role
   const int l = tid & 63, g = l >> 4, li = l & 15;
   const bool has_rows = is_qk && w < RB;
-  const int part = blockIdx.x, rbk = blockIdx.y;
+  const int part = blockIdx.x;
+  // several KV heads: grid.y = h_kv * row blocks per head; the Mkv = s_q * G
+  // rows of KV head kvh (G = h_q / h_kv query heads each) are numbered
+  // s * G + hh, and are row s * h_q + kvh * G + hh of the request
+  const int nrb = MKV ? (a.Mkv + MB - 1) / MB : 1;
+  const int kvh = MKV ? (int)blockIdx.y / nrb : 0;
+  const int rbk = MKV ? (int)blockIdx.y - kvh * nrb : (int)blockIdx.y;
+  const int Mloc = MKV ? a.Mkv : a.M;
+  const int Gq = MKV ? a.G : a.h_q;
+  auto grow = [&](int rho) -> int {
+    if constexpr (MKV) return (rho / a.G) * a.h_q + kvh * a.G + rho % a.G;
+    else return rho;
+  };
   const int begin_req = ld_const(a.sched_meta, part * 8 + 0);
   if (begin_req < 0) return;
   const int begin_blk = ld_const(a.sched_meta, part * 8 + 1);
@@ -921,6 +968,11 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
 
   TileLoader<false> loader;
   loader.init(w, l);  // used by the QK waves (4 waves split a tile)
+  if constexpr (MKV) loader.init_rows(w, l);
+  auto issue_tile = [&](int64_t page, int key0, int st) {
+    if constexpr (MKV) loader.issue_page_hkv(a, page, key0, kvh, smem, st, w);
+    else loader.issue_page(a, page, key0, smem, st, w);
+  };
   const int kx = li & 7;
   const uint32_t kq_base0 = (uint32_t)(li * kRowBytes + 16 * (4 * (0 ^ (kx >> 2)) + (g ^ (kx & 3))));
   const uint32_t kq_base1 = (uint32_t)(li * kRowBytes + 16 * (4 * (1 ^ (kx >> 2)) + (g ^ (kx & 3))));
@@ -975,10 +1027,10 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
 
     if (is_qk) {
       // ================================================================ QK waves
-      const bool live = has_rows && rho < a.M;
+      const bool live = has_rows && rho < Mloc;
       bf16x8 qreg[18];
       {
-        const uint16_t* qrow = a.q + ((int64_t)r * a.M + (live ? rho : 0)) * kDQK + 8 * g;
+        const uint16_t* qrow = a.q + ((int64_t)r * a.M + (live ? grow(rho) : 0)) * kDQK + 8 * g;
 #pragma unroll
         for (int s = 0; s < 18; ++s) {
           const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 32 * s);
@@ -988,7 +1040,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
       int lim = 0;
       if (live) {
         int nvis = seqlen;
-        if (a.causal) nvis = min(max(seqlen - a.s_q + rho / a.h_q + 1, 0), seqlen);
+        if (a.causal) nvis = min(max(seqlen - a.s_q + rho / Gq + 1, 0), seqlen);
         lim = min(t1, nvis);
       }
       float mrow = -INFINITY, lpart = 0.f;
@@ -1090,8 +1142,8 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
       // before the PV waves do, so the issue stalls of the vector-memory path
       // cost less on them.  Tiles 0 and 1 now, tile t+2 at the start of
       // iteration t.
-      if (ntile > 0) loader.issue_page(a, uniform(page_raw(0)), t0, smem, 0, w);
-      if (ntile > 1) loader.issue_page(a, uniform(page_raw(1)), t0 + kTK, smem, 1, w);
+      if (ntile > 0) issue_tile(uniform(page_raw(0)), t0, 0);
+      if (ntile > 1) issue_tile(uniform(page_raw(1)), t0 + kTK, 1);
       // page id of the tile the next iteration loads: read before the barrier that
       // ends an iteration (which waits for it) and made wave-uniform after it
       int pg_next = ntile > 2 ? page_raw(2) : 0;
@@ -1107,7 +1159,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
         // loads of tile t+2 into the slot of tile t-2 (its K was read in
         // iteration t-2, its V in iteration t-1)
         const bool more = t + 2 < ntile;
-        if (more) loader.issue_page(a, uniform(pg_next), t0 + (t + 2) * kTK, smem, (t + 2) & 3, w);
+        if (more) issue_tile(uniform(pg_next), t0 + (t + 2) * kTK, (t + 2) & 3);
         if (has_rows) {
           if constexpr (DO_QK) {
             f32x4 acc[2];
@@ -1131,10 +1183,10 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
             const float lt = row4_sum(lpart);
             if (g == 0) {
               l_s[row_local] = lt;
-              if (rho < a.M) {
+              if (rho < Mloc) {
                 const float lse = lt > 0.f ? (mrow + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
-                if (nsplit == 1) a.lse[(int64_t)r * a.M + rho] = lse;
-                else a.part_lse[(int64_t)slot * a.M + rho] = lse;
+                if (nsplit == 1) a.lse[(int64_t)r * a.M + grow(rho)] = lse;
+                else a.part_lse[(int64_t)slot * a.M + grow(rho)] = lse;
               }
             }
           }
@@ -1244,8 +1296,9 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
       sync_lds();  // l from the QK waves (written in iteration ntile)
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const int rho_o = rbk * MB + 16 * rb + li;
-        if (rho_o >= a.M) continue;
+        const int rho_l = rbk * MB + 16 * rb + li;
+        if (rho_l >= Mloc) continue;
+        const int rho_o = grow(rho_l);
         const float lt = l_s[16 * rb + li];
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         if (nsplit == 1) {
@@ -1284,20 +1337,25 @@ int decode_row_blocks_per_wg(int M) {
 template <int RB>
 static hipError_t launch_decode_t(const DecodeArgs& a, int kind, hipStream_t stream) {
   const int MB = 16 * RB;
-  dim3 grid(a.num_parts, (a.M + MB - 1) / MB);
+  const bool mkv = a.h_kv > 1;
+  dim3 grid(a.num_parts, mkv ? a.h_kv * ((a.Mkv + MB - 1) / MB) : (a.M + MB - 1) / MB);
   if (kind == kDecodeFp8Packed)
     hipLaunchKernelGGL((decode_kernel<RB, true, false>), grid, dim3(kDecodeThreads), 0, stream, a);
   else if (kind == kDecodeFp8Indexed)
     hipLaunchKernelGGL((decode_kernel<RB, true, true>), grid, dim3(kDecodeThreads), 0, stream, a);
+  else if (kind == kDecodeF16 && mkv)
+    hipLaunchKernelGGL((decode_ws_kernel<RB, true, true>), grid, dim3(kWsThreads), 0, stream, a);
   else if (kind == kDecodeF16)
-    hipLaunchKernelGGL((decode_ws_kernel<RB, true>), grid, dim3(kWsThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_ws_kernel<RB, true, false>), grid, dim3(kWsThreads), 0, stream, a);
+  else if (mkv)
+    hipLaunchKernelGGL((decode_ws_kernel<RB, false, true>), grid, dim3(kWsThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_ws_kernel<RB, false>), grid, dim3(kWsThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_ws_kernel<RB, false, false>), grid, dim3(kWsThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int kind, hipStream_t stream) {
-  switch (decode_row_blocks_per_wg(a.M)) {
+  switch (decode_row_blocks_per_wg(a.h_kv > 1 ? a.Mkv : a.M)) {
     case 1: return launch_decode_t<1>(a, kind, stream);
     case 2: return launch_decode_t<2>(a, kind, stream);
     default: return launch_decode_t<4>(a, kind, stream);
@@ -1310,9 +1368,10 @@ static hipError_t occupancy_t(int kind, int* n) {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_kernel<RB, true, false>, kDecodeThreads, 0);
   if (kind == kDecodeFp8Indexed)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_kernel<RB, true, true>, kDecodeThreads, 0);
+  // (the several-KV-head instantiations use the same registers and LDS)
   if (kind == kDecodeF16)
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_ws_kernel<RB, true>, kWsThreads, 0);
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_ws_kernel<RB, false>, kWsThreads, 0);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_ws_kernel<RB, true, false>, kWsThreads, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_ws_kernel<RB, false, false>, kWsThreads, 0);
 }
 
 hipError_t decode_occupancy(int kind, int M, int* wgs_per_cu) {

@@ -44,7 +44,7 @@ _i32, _i64, _f32, _sz = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_s
 _SIGS = {
     "mla_last_error_message": ([], ctypes.c_char_p),
     "mla_decode_num_parts": ([_i32, _i32, _i32, _i32, _i32, _P], _i32),
-    "mla_plan_num_parts": ([_i32, _i32, _i32, _i32, _i32, _i32, _P], _i32),
+    "mla_plan_num_parts": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32, _P], _i32),
     "mla_decode_workspace_size": ([_i32, _i32, _i32, _i32], _sz),
     "mla_packed_kv_workspace_size": ([_i32, _i32, _i32], _sz),
     "mla_get_decode_metadata": ([_P, _i32, _i32, _i32, _i32, _i32, _P, _P, _P], _i32),
@@ -110,9 +110,9 @@ def mla_decode_num_parts(batch, s_q, h_q, h_kv=1, kv_format=KV_BF16_PAGED) -> in
     return out.value
 
 
-def mla_plan_num_parts(batch, s_q, h_q, kv_format, cus, wgs_per_cu) -> int:
+def mla_plan_num_parts(batch, s_q, h_q, kv_format, cus, wgs_per_cu, h_kv=1) -> int:
     out = ctypes.c_int(0)
-    _check(_lib.mla_plan_num_parts(batch, s_q, h_q, kv_format, cus, wgs_per_cu, ctypes.byref(out)))
+    _check(_lib.mla_plan_num_parts(batch, s_q, h_q, h_kv, kv_format, cus, wgs_per_cu, ctypes.byref(out)))
     return out.value
 
 
@@ -149,10 +149,12 @@ def mla_decode_fwd(q, kv, kv_format, block_table, seqlens, softmax_scale, causal
     b, s_q, h_q, d = q.shape
     if d != D_QK:
         raise ValueError(f"q last dim {d}, expected {D_QK}")
+    h_kv = 1
     if kv_format in (KV_BF16_PAGED, KV_FP16_PAGED):
         _need(kv, "kcache", _act_dtype(kv_format))
-        if tuple(kv.shape[1:]) != (PAGE, 1, D_QK):
-            raise ValueError(f"kcache shape {tuple(kv.shape)}, expected [pages, 64, 1, 576]")
+        if kv.dim() != 4 or kv.shape[1] != PAGE or kv.shape[3] != D_QK:
+            raise ValueError(f"kcache shape {tuple(kv.shape)}, expected [pages, 64, h_kv, 576]")
+        h_kv = kv.shape[2]
         _need(block_table, "block_table", torch.int32)
         if block_table.dim() != 2 or block_table.shape[0] != b:
             raise ValueError("block_table must be [batch, max_pages]")
@@ -181,7 +183,7 @@ def mla_decode_fwd(q, kv, kv_format, block_table, seqlens, softmax_scale, causal
     _need(workspace, "workspace", torch.uint8)
     _check(_lib.mla_decode_fwd(
         _ptr(q), _ptr(kv), kv_format, num_pages, _ptr(block_table) if kv_format != KV_FP8_PACKED else None,
-        max_pages, _ptr(seqlens), topk_capacity, b, s_q, h_q, 1, float(softmax_scale), int(bool(causal)),
+        max_pages, _ptr(seqlens), topk_capacity, b, s_q, h_q, h_kv, float(softmax_scale), int(bool(causal)),
         _ptr(sched_meta), _ptr(num_splits), sched_meta.shape[0], _ptr(out), _ptr(lse), _ptr(workspace),
         workspace.numel(), _stream(stream)))
 
@@ -251,10 +253,10 @@ class DecodePlan:
     Built once per step (the metadata depends only on the lengths) and reused by
     every layer of that step, as the scheduler metadata is meant to be."""
 
-    def __init__(self, seqlens, s_q, h_q, kv_format=KV_BF16_PAGED, num_parts=None, stream=None):
+    def __init__(self, seqlens, s_q, h_q, kv_format=KV_BF16_PAGED, num_parts=None, stream=None, h_kv=1):
         b = seqlens.shape[0]
         self.batch, self.s_q, self.h_q, self.kv_format = b, s_q, h_q, kv_format
-        self.num_parts = int(num_parts) if num_parts else mla_decode_num_parts(b, s_q, h_q, 1, kv_format)
+        self.num_parts = int(num_parts) if num_parts else mla_decode_num_parts(b, s_q, h_q, h_kv, kv_format)
         self.sched_meta, self.num_splits = mla_get_decode_metadata(seqlens, b, s_q, h_q, 1, self.num_parts,
                                                                    stream=stream)
         nbytes = mla_decode_workspace_size(b, s_q, h_q, self.num_parts)
@@ -268,7 +270,8 @@ def mla_decode(q, kv, block_table, seqlens, softmax_scale=None, causal=False, pl
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D_QK)
     if plan is None:
-        plan = DecodePlan(seqlens, s_q, h_q, kv_format, stream=stream)
+        h_kv = kv.shape[2] if kv_format in (KV_BF16_PAGED, KV_FP16_PAGED) else 1
+        plan = DecodePlan(seqlens, s_q, h_q, kv_format, stream=stream, h_kv=h_kv)
     if out is None:
         out = torch.empty((b, s_q, h_q, D_V), dtype=_act_dtype(kv_format), device=q.device)
     if lse is None:

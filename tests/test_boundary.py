@@ -64,6 +64,16 @@ def test_plan_num_parts(batch, s_q, h_q, cus, wgs, expect):
     assert ops.mla_plan_num_parts(batch, s_q, h_q, ops.KV_BF16_PAGED, cus, wgs) == expect
 
 
+@pytest.mark.parametrize("batch,s_q,h_q,h_kv", [(64, 1, 128, 2), (64, 1, 128, 4), (8, 2, 64, 4), (1, 1, 64, 4)])
+def test_plan_num_parts_multi_kv_head(batch, s_q, h_q, h_kv):
+    """Row blocks are counted per KV head: h_kv * ceil(s_q * h_q / h_kv / rows per workgroup)."""
+    mkv = s_q * (h_q // h_kv)
+    rb = 16 * (1 if mkv <= 16 else 2 if mkv <= 32 else 4)
+    row_blocks = h_kv * ((mkv + rb - 1) // rb)
+    want = min(max(256 // row_blocks, 1), batch * 16)
+    assert ops.mla_plan_num_parts(batch, s_q, h_q, ops.KV_BF16_PAGED, 256, 1, h_kv=h_kv) == want
+
+
 def decode_call(**kw):
     args = dict(q=FAKE, kv=FAKE, fmt=ops.KV_BF16_PAGED, num_pages=16, bt=FAKE, max_pages=4, seqlens=FAKE, cap=0,
                 batch=2, s_q=1, h_q=128, h_kv=1, scale=0.04, causal=0, meta=FAKE, ns=FAKE, parts=8, out=FAKE,
@@ -77,12 +87,15 @@ def decode_call(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(h_kv=2), ops.MLA_ERR_UNSUPPORTED),
+    (dict(h_kv=3), ops.MLA_ERR_UNSUPPORTED),              # does not divide h_q = 128
+    (dict(h_kv=0), ops.MLA_ERR_UNSUPPORTED),
+    (dict(h_kv=32, h_q=128), ops.MLA_ERR_UNSUPPORTED),    # above 16
+    (dict(fmt=ops.KV_FP8_PACKED, cap=2048, h_q=128, h_kv=2), ops.MLA_ERR_UNSUPPORTED),
     (dict(h_q=17), ops.MLA_ERR_UNSUPPORTED),
     (dict(h_q=144), ops.MLA_ERR_UNSUPPORTED),
     (dict(s_q=17, h_q=128), ops.MLA_ERR_UNSUPPORTED),     # 2176 rows > 2048
     (dict(fmt=7), ops.MLA_ERR_UNSUPPORTED),
-    (dict(fmt=ops.KV_FP16_PAGED, h_kv=2), ops.MLA_ERR_UNSUPPORTED),
+    (dict(fmt=ops.KV_FP16_PAGED, h_kv=5), ops.MLA_ERR_UNSUPPORTED),
     (dict(fmt=ops.KV_FP16_PAGED, h_q=136), ops.MLA_ERR_UNSUPPORTED),
     (dict(fmt=ops.KV_FP16_PAGED, bt=NULL), ops.MLA_ERR_INVALID_ARGUMENT),
     (dict(fmt=ops.KV_FP8_PACKED, cap=2048, h_q=96), ops.MLA_ERR_UNSUPPORTED),
@@ -131,8 +144,8 @@ def test_metadata_and_combine_and_pack_fail_closed():
     assert lib.mla_pack_selected_kv(FAKE, 0, FAKE, FAKE, 2, 1, 128, FAKE, 1 << 40, NULL) == ops.MLA_ERR_INVALID_ARGUMENT
     assert "multiple of 64" in ops.mla_last_error_message() or ops.mla_last_error_message()
     out = ctypes.c_int(0)
-    assert lib.mla_plan_num_parts(1, 1, 128, 0, 0, 1, ctypes.byref(out)) == ops.MLA_ERR_INVALID_ARGUMENT
-    assert lib.mla_decode_num_parts(1, 1, 128, 2, 0, ctypes.byref(out)) == ops.MLA_ERR_UNSUPPORTED
+    assert lib.mla_plan_num_parts(1, 1, 128, 1, 0, 0, 1, ctypes.byref(out)) == ops.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_decode_num_parts(1, 1, 128, 3, 0, ctypes.byref(out)) == ops.MLA_ERR_UNSUPPORTED
 
 
 def test_sparse_kv_format_policy():

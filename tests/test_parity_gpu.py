@@ -103,6 +103,42 @@ def test_dense_fp16(case):
     G.compare(name, out, lse, *oracle_dense(w))
 
 
+DENSE_MULTI_KV = [
+    # name, seed, b, s_q, h_q, h_kv, seqlens, pool pages, causal, forced parts, dtype
+    ("hkv2-h128", 130, 3, 1, 128, 2, [1, 700, 2049], 60, False, None, "bf16"),
+    ("hkv4-h128-p5", 131, 2, 1, 128, 4, [300, 1000], 24, False, 5, "bf16"),
+    ("hkv4-h64-causal-sq3", 132, 2, 3, 64, 4, [5, 400], 10, True, None, "bf16"),
+    ("hkv3-h48", 133, 2, 1, 48, 3, [129, 64], 6, False, None, "bf16"),
+    ("hkv2-h128-fp16", 134, 2, 2, 128, 2, [64, 900], 20, True, 3, "fp16"),
+]
+
+
+@pytest.mark.parametrize("case", DENSE_MULTI_KV, ids=[c[0] for c in DENSE_MULTI_KV])
+def test_dense_multi_kv_head(case):
+    """Several KV heads against the oracle, and each query-head group bitwise
+    equal to an h_kv = 1 decode of that group over its own KV head."""
+    name, seed, b, s_q, h_q, h_kv, seqlens, pool, causal, parts, dtype = case
+    G.say(f"dense multi-KV-head {name}")
+    w = W.dense_workload(name, seed, b, s_q, h_q, seqlens, pool_pages=pool, causal=causal, num_parts=parts,
+                         dtype=dtype, h_kv=h_kv)
+    t = G.dev_tensors(w)
+    fmt = ops.KV_FP16_PAGED if dtype == "fp16" else ops.KV_BF16_PAGED
+    P = parts or ops.mla_decode_num_parts(b, s_q, h_q, h_kv, fmt)
+    plan = ops.DecodePlan(t["seqlens"], s_q, h_q, fmt, num_parts=P, h_kv=h_kv)
+    out, lse = ops.mla_decode(t["q"], t["kcache"], t["block_table"], t["seqlens"], w.scale, w.causal, plan=plan,
+                              kv_format=fmt)
+    torch.cuda.synchronize()
+    G.compare(name, out, lse, *oracle_dense(w))
+    g = h_q // h_kv
+    for kk in range(h_kv):
+        qg = t["q"][:, :, kk * g:(kk + 1) * g].contiguous()
+        kg = t["kcache"][:, :, kk:kk + 1].contiguous()
+        plan1 = ops.DecodePlan(t["seqlens"], s_q, g, fmt, num_parts=P)
+        o1, l1 = ops.mla_decode(qg, kg, t["block_table"], t["seqlens"], w.scale, w.causal, plan=plan1, kv_format=fmt)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, out[:, :, kk * g:(kk + 1) * g]) and torch.equal(l1, lse[:, :, kk * g:(kk + 1) * g])
+
+
 @pytest.mark.parametrize("cfg", ["c1", "c2"])
 def test_named_small_configs(cfg):
     G.say(f"config {cfg}")
