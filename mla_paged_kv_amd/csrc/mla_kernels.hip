@@ -1405,20 +1405,52 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
     return;
   }
   uint16_t* orow = out + ((int64_t)r * M + rho) * kDV + 8 * l;
+  // the split lse values, 64 at a time, one per lane: max and sum by wave reductions
   float mx = -INFINITY;
-  for (int i = 0; i < S; ++i) mx = fmaxf(mx, part_lse[(int64_t)(s0 + i) * M + rho]);
+  for (int i0 = 0; i0 < S; i0 += 64) {
+    const float v = i0 + l < S ? part_lse[(int64_t)(s0 + i0 + l) * M + rho] : -INFINITY;
+    mx = fmaxf(mx, v);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
   if (mx == -INFINITY) {  // no split saw a key (or no split at all)
     *reinterpret_cast<u32x4*>(orow) = u32x4{0u, 0u, 0u, 0u};
     if (l == 0) lse[(int64_t)r * M + rho] = -INFINITY;
     return;
   }
   float tot = 0.f;
-  for (int i = 0; i < S; ++i) tot += expf(part_lse[(int64_t)(s0 + i) * M + rho] - mx);
+  for (int i0 = 0; i0 < S; i0 += 64) {
+    const float v = i0 + l < S ? part_lse[(int64_t)(s0 + i0 + l) * M + rho] : -INFINITY;
+    tot += expf(v - mx);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
   const float L = mx + logf(tot);
+  // weighted sum of the partial rows; lane l owns columns [8l, 8l+8).  Four
+  // splits per step so that their loads are in flight together.
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < S; ++i) {
+  const float* src0 = part_o + ((int64_t)s0 * M + rho) * kDV + 8 * l;
+  const int64_t stride = (int64_t)M * kDV;
+  int i = 0;
+  for (; i + 4 <= S; i += 4) {
+    f32x4 a[4], b[4];
+    float wgt[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float* src = src0 + (int64_t)(i + u) * stride;
+      a[u] = *reinterpret_cast<const f32x4*>(src);
+      b[u] = *reinterpret_cast<const f32x4*>(src + 4);
+      wgt[u] = expf(part_lse[(int64_t)(s0 + i + u) * M + rho] - L);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      acc0 += wgt[u] * a[u];
+      acc1 += wgt[u] * b[u];
+    }
+  }
+  for (; i < S; ++i) {
+    const float* src = src0 + (int64_t)i * stride;
     const float wgt = expf(part_lse[(int64_t)(s0 + i) * M + rho] - L);
-    const float* src = part_o + ((int64_t)(s0 + i) * M + rho) * kDV + 8 * l;
     acc0 += wgt * *reinterpret_cast<const f32x4*>(src);
     acc1 += wgt * *reinterpret_cast<const f32x4*>(src + 4);
   }
