@@ -42,9 +42,13 @@ int hip_fail(hipError_t e, const char* what) {
 // Empirical partition gate: at most this many pieces per request.  Each extra
 // piece re-reads the request's Q rows, runs a prologue/epilogue and writes a
 // 128 x 513 fp32 partial that the combine re-reads, so splitting finer than
-// the occupancy needs costs bandwidth.  EMPIRICAL: an initial value, not
-// derived; it is meant to be re-read off an MI355X sweep of the decode kernel.
+// the occupancy needs costs bandwidth.  Measured on MI355X (HIP-graph step,
+// metadata + decode + combine): for the bf16 kernel 16 and 32 pieces per
+// request are within +-4 % at b = 1..16, sk = 1024..8192, and 64 is slower at
+// b = 1; the FP8 kernel is slower per tile and gains from finer pieces (C5:
+// 45.9 us at 16 per request, 38.7 us at 32, 38.5 us at 64).
 constexpr int kMaxSplitsPerRequest = 16;
+constexpr int kMaxSplitsPerRequestFp8 = 32;
 
 bool is_gfx950() {
   static int cache[64];  // 0 unknown, 1 gfx950, 2 other (benign race: same value written)
@@ -107,7 +111,8 @@ int mla_plan_num_parts(int batch, int s_q, int h_q, int h_kv, int kv_format, int
   int64_t slots = (int64_t)cus * wgs_per_cu;
   int64_t parts = slots / row_blocks;
   if (parts < 1) parts = 1;
-  const int64_t cap = (int64_t)batch * kMaxSplitsPerRequest;
+  const bool fp8 = kv_format == MLA_KV_FP8_PACKED || kv_format == MLA_KV_FP8_INDEXED;
+  const int64_t cap = (int64_t)batch * (fp8 ? kMaxSplitsPerRequestFp8 : kMaxSplitsPerRequest);
   if (parts > cap) parts = cap;
   if (parts > MLA_MAX_PARTS) parts = MLA_MAX_PARTS;
   *num_parts_out = (int)parts;

@@ -64,6 +64,15 @@ def test_plan_num_parts(batch, s_q, h_q, cus, wgs, expect):
     assert ops.mla_plan_num_parts(batch, s_q, h_q, ops.KV_BF16_PAGED, cus, wgs) == expect
 
 
+@pytest.mark.parametrize("fmt,batch,s_q,h_q,expect", [
+    (ops.KV_FP8_PACKED, 8, 1, 64, 256),     # one row block per request; 32 pieces per request allowed
+    (ops.KV_FP8_INDEXED, 2, 1, 128, 64),    # two row blocks: 128 slots, capped at 2 x 32
+    (ops.KV_BF16_PAGED, 8, 1, 64, 128),     # the bf16 kernel keeps 16 per request
+])
+def test_plan_num_parts_fp8_cap(fmt, batch, s_q, h_q, expect):
+    assert ops.mla_plan_num_parts(batch, s_q, h_q, fmt, 256, 1) == expect
+
+
 @pytest.mark.parametrize("batch,s_q,h_q,h_kv", [(64, 1, 128, 2), (64, 1, 128, 4), (8, 2, 64, 4), (1, 1, 64, 4)])
 def test_plan_num_parts_multi_kv_head(batch, s_q, h_q, h_kv):
     """Row blocks are counted per KV head: h_kv * ceil(s_q * h_q / h_kv / rows per workgroup)."""
