@@ -297,3 +297,42 @@ def sched_partition(lengths, num_parts):
         er, ek = where[mine[-1]]
         meta[p, :5] = [br, bk, er, ek + 1, p - first_part[br]]
     return meta, num_splits
+
+
+def sched_partition_request_local(lengths, num_parts):
+    """Request-local partition (the "compact request-local scheduler" of "[SM90]
+    Add packed selected-KV sparse decode", Scheduler policy; the page names it
+    without defining it, so this is the reading: no part spans two requests).
+
+    blocks_r = ceil(len_r / 64).  If more requests have a block than there are
+    parts, returns None (the form needs one part per such request).  Otherwise
+    B = the smallest piece size in blocks with sum_r ceil(blocks_r / B) <= P;
+    request r gets n_r = ceil(blocks_r / B) pieces, piece i covering blocks
+    [floor(i * b_r / n_r), floor((i + 1) * b_r / n_r)); parts are numbered in
+    (request, piece) order and the parts after the last piece are empty.
+    Same output format as sched_partition.
+    """
+    lengths = [max(int(x), 0) for x in lengths]
+    P = int(num_parts)
+    assert P >= 1
+    blocks = [(n + PAGE - 1) // PAGE for n in lengths]
+    T = sum(blocks)
+    nonempty = sum(1 for x in blocks if x)
+    if nonempty > P:
+        return None
+    meta = np.zeros((P, 8), np.int32)
+    meta[:, :5] = -1
+    num_splits = np.zeros(len(lengths) + 1, np.int32)
+    if T == 0:
+        return meta, num_splits
+    B = (T + P - 1) // P
+    while sum((x + B - 1) // B for x in blocks) > P:
+        B += 1
+    part = 0
+    for r, nb in enumerate(blocks):
+        n = (nb + B - 1) // B
+        for i in range(n):
+            meta[part, :5] = [r, (i * nb) // n, r, ((i + 1) * nb) // n, i]
+            part += 1
+        num_splits[r + 1] = num_splits[r] + n
+    return meta, num_splits

@@ -379,6 +379,52 @@ def test_sched_partition_invariants(lengths, P):
     assert ns[-1] <= sum(1 for x in blocks if x) + P - 1
 
 
+@pytest.mark.parametrize("lengths,P", [
+    ([2048] * 8, 256), ([1536, 2048, 1700, 1600], 64), ([1, 64, 65, 0, 300], 4), ([0, 0], 3), ([10], 5),
+    ([2048, 4096, 3000, 100], 9), ([64] * 5, 5), ([128, 64], 2), ([4096], 256), ([700, 0, 2049], 7),
+    (list(np.random.default_rng(5).integers(0, 3000, size=40)), 128),
+])
+def test_request_local_partition_invariants(lengths, P):
+    res = O.sched_partition_request_local(lengths, P)
+    blocks = [(max(n, 0) + 63) // 64 for n in lengths]
+    assert res is not None
+    meta, ns = res
+    T = sum(blocks)
+    owned = [np.zeros(b, int) for b in blocks]
+    pieces = {}
+    used = 0
+    for p in range(P):
+        br, bk, er, ek, i = meta[p, :5]
+        assert np.all(meta[p, 5:] == 0)
+        if br < 0:
+            assert np.all(meta[p, :5] == -1)
+            assert all(meta[q, 0] < 0 for q in range(p, P))  # empty parts only trail
+            break
+        used += 1
+        assert br == er and ek > bk  # never spans two requests
+        owned[br][bk:ek] += 1
+        pieces.setdefault(br, []).append((i, ek - bk, p))
+    assert all(np.all(o == 1) for o in owned)  # every block exactly once
+    assert used <= P and ns[-1] == used
+    for r, nb in enumerate(blocks):
+        got = sorted(pieces.get(r, []))
+        assert ns[r + 1] - ns[r] == len(got)
+        if nb:
+            assert [g[0] for g in got] == list(range(len(got)))                    # split index in order
+            assert [g[2] for g in got] == list(range(ns[r], ns[r] + len(got)))   # consecutive parts
+            sizes = [g[1] for g in got]
+            assert max(sizes) - min(sizes) <= 1                                    # balanced within the request
+    # piece counts: ceil(b_r / B) for the smallest B (searched from 1 here) that fits in P parts
+    if T:
+        B = next(x for x in range(1, max(blocks) + 1) if sum((b + x - 1) // x for b in blocks) <= P)
+        assert all(ns[r + 1] - ns[r] == (b + B - 1) // B for r, b in enumerate(blocks))
+
+
+def test_request_local_partition_needs_a_part_per_request():
+    assert O.sched_partition_request_local([64, 64, 64], 2) is None
+    assert O.sched_partition_request_local([64, 0, 64], 2) is not None
+
+
 # ----------------------------------------------------------------------------- numbers the pages print
 
 def test_page_byte_facts():
