@@ -292,9 +292,13 @@ def sparse_main(args):
         lse = torch.empty((b, s_q, h_q), dtype=torch.float32, device=dev)
         plans = {f: ops.DecodePlan(t["seqlens"], s_q, h_q, f) for f in (ops.KV_FP8_INDEXED, ops.KV_FP8_PACKED)}
 
-        def decode(fmt):
+        def decode(fmt, policy=None):
             p = plans[fmt]
-            ops.mla_get_decode_metadata(t["seqlens"], b, s_q, h_q, 1, p.num_parts, p.sched_meta, p.num_splits)
+            if policy is None:
+                ops.mla_get_decode_metadata(t["seqlens"], b, s_q, h_q, 1, p.num_parts, p.sched_meta, p.num_splits)
+            else:
+                ops.mla_get_packed_decode_metadata(t["seqlens"], b, s_q, h_q, cap, p.num_parts, policy, p.sched_meta,
+                                                   p.num_splits)
             kv, ix = (t["kcache_rec"], t["indices"]) if fmt == ops.KV_FP8_INDEXED else (ws, None)
             ops.mla_decode_fwd(t["q"], kv, fmt, ix, t["seqlens"], w.scale, False, p.sched_meta, p.num_splits, out,
                                lse, p.workspace, topk_capacity=cap)
@@ -307,6 +311,7 @@ def sparse_main(args):
             "patch_then_packed": lambda: (ops.mla_patch_packed_kv(t["kcache_rec"], t["indices"], t["seqlens"], ids,
                                                                   ws),
                                           decode(ops.KV_FP8_PACKED)),
+            "by_index_request_local_sched": lambda: decode(ops.KV_FP8_INDEXED, ops.SCHED_REQUEST_LOCAL),
         }
         ref_o, ref_l = orc.mla_sparse_decode(w.q_bits, w.kcache_rec, w.indices, w.seqlens, w.scale,
                                              nthreads=orc.default_threads())

@@ -142,6 +142,36 @@ size_t mla_packed_kv_workspace_size(int batch, int s_q, int topk_capacity);
 int mla_get_decode_metadata(const int32_t* seqlens, int batch, int s_q, int h_q, int h_kv, int num_parts,
                             int32_t* sched_meta, int32_t* num_splits, void* stream);
 
+/* Scheduler policies of mla_get_packed_decode_metadata. */
+typedef enum {
+  MLA_SCHED_AUTO = 0,          /* the hybrid policy described below */
+  MLA_SCHED_GLOBAL = 1,        /* the partition of mla_get_decode_metadata */
+  MLA_SCHED_REQUEST_LOCAL = 2  /* no partition spans two requests */
+} mla_sched_policy;
+
+/* Scheduler metadata for the sparse FP8 paths (device, one workgroup), the
+ * get_packed_mla_metadata call of "[SM90] Add packed selected-KV sparse
+ * decode" (FlashMLA PR 200, Python API, Scheduler policy).  Same outputs and
+ * format as mla_get_decode_metadata, over topk_length.
+ *   MLA_SCHED_GLOBAL: exactly mla_get_decode_metadata's partition.
+ *   MLA_SCHED_REQUEST_LOCAL: the page's "compact request-local scheduler",
+ *     which it names without defining; here: with b_r = ceil(topk_length[r] /
+ *     64) blocks, B = the smallest piece size with sum_r ceil(b_r / B) <=
+ *     num_parts; request r is cut into ceil(b_r / B) balanced pieces (piece i =
+ *     blocks [floor(i b_r / n_r), floor((i+1) b_r / n_r))), partitions follow in
+ *     (request, piece) order and the rest are empty.  If more requests have a
+ *     block than there are partitions, the global partition is produced.
+ *   MLA_SCHED_AUTO: the page picks request-local for H = 64 outside a
+ *     fallback regime on its GPU; on MI355X the global partition measured
+ *     faster at every tested shape (h_q 64/128, batch * s_q 1..32), so AUTO
+ *     is the global partition.
+ * topk_length (device) int32 [batch]; sched_meta (device) [num_parts][8];
+ * num_splits (device) [batch + 1]; h_q 64 or 128; topk_capacity a positive
+ * multiple of 64. */
+int mla_get_packed_decode_metadata(const int32_t* topk_length, int batch, int s_q, int h_q, int topk_capacity,
+                                   int num_parts, int policy, int32_t* sched_meta, int32_t* num_splits,
+                                   void* stream);
+
 /* Decode (device).  Launches num_parts x h_kv * ceil(s_q*h_q/h_kv / R) workgroups
  * (R = 16, 32 or 64 query rows of one KV head per workgroup); each walks its
  * partition's pages with an

@@ -48,7 +48,7 @@ struct DecodeArgs {
 int decode_row_blocks_per_wg(int M);
 
 hipError_t launch_sched(const int32_t* lengths, int batch, int num_parts, int32_t* meta, int32_t* num_splits,
-                        hipStream_t stream);
+                        hipStream_t stream, bool request_local = false);
 // Decode kernel family: bf16 pages, FP8 packed workspace, FP8 pool gathered by
 // index, fp16 pages.
 enum DecodeKind { kDecodeBf16 = 0, kDecodeFp8Packed = 1, kDecodeFp8Indexed = 2, kDecodeF16 = 3 };

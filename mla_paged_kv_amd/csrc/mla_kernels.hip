@@ -268,6 +268,93 @@ __device__ __forceinline__ int block_excl_scan(int local, int* total, int32_t* w
   return base + incl - local;
 }
 
+// workgroup-wide max of a non-negative int (every thread gets it)
+__device__ __forceinline__ int block_max(int v, int32_t* wsum) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
+  if (lane == 0) wsum[wv] = v;
+  __syncthreads();
+  int m = 0;
+#pragma unroll
+  for (int i = 0; i < kSchedThreads / 64; ++i) m = max(m, wsum[i]);
+  __syncthreads();  // wsum is reused
+  return m;
+}
+
+// Request-local partition (no part spans two requests; see mla_paged_kv.h):
+// B = the smallest piece size in blocks with sum_r ceil(b_r / B) <= num_parts,
+// request r in ceil(b_r / B) balanced pieces, parts in (request, piece) order.
+// Returns false, having written nothing, when more requests have a block than
+// there are parts.  bl[r] = blocks of request r (LDS), filled by the caller.
+__device__ bool request_local_partition(const int32_t* bl, int batch, int num_parts, int32_t* meta,
+                                        int32_t* num_splits, int32_t* wsum) {
+  const int t = threadIdx.x;
+  const int C = (batch + kSchedThreads - 1) / kSchedThreads;
+  int nonempty = 0, maxb = 0, tot_local = 0;
+  for (int k = 0; k < C; ++k) {
+    const int r = t * C + k;
+    if (r < batch) {
+      nonempty += bl[r] > 0;
+      maxb = max(maxb, bl[r]);
+      tot_local += bl[r];
+    }
+  }
+  int N = 0, T = 0;
+  block_excl_scan(nonempty, &N, wsum);
+  block_excl_scan(tot_local, &T, wsum);
+  maxb = block_max(maxb, wsum);
+  if (N > num_parts) return false;
+  int B = maxb;  // sum_r ceil(b_r / maxb) = N <= num_parts
+  if (T > 0) {
+    int lo = (T + num_parts - 1) / num_parts, hi = maxb;  // smallest B in [lo, hi] that fits
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      int cnt = 0;
+      for (int k = 0; k < C; ++k) {
+        const int r = t * C + k;
+        if (r < batch) cnt += (bl[r] + mid - 1) / mid;
+      }
+      int total = 0;
+      block_excl_scan(cnt, &total, wsum);
+      if (total <= num_parts) hi = mid; else lo = mid + 1;
+    }
+    B = lo;
+  }
+  int pieces_local = 0;
+  for (int k = 0; k < C; ++k) {
+    const int r = t * C + k;
+    if (r < batch && T > 0) pieces_local += (bl[r] + B - 1) / B;
+  }
+  int used = 0;
+  int off = block_excl_scan(pieces_local, &used, wsum);
+  for (int k = 0; k < C; ++k) {
+    const int r = t * C + k;
+    if (r >= batch) break;
+    num_splits[r] = off;
+    const int b = bl[r];
+    const int n = T > 0 ? (b + B - 1) / B : 0;
+    for (int i = 0; i < n; ++i) {
+      int32_t* m = meta + (int64_t)(off + i) * 8;
+      m[0] = r;
+      m[1] = (int32_t)(((int64_t)i * b) / n);
+      m[2] = r;
+      m[3] = (int32_t)(((int64_t)(i + 1) * b) / n);
+      m[4] = i;
+      m[5] = m[6] = m[7] = 0;
+    }
+    off += n;
+  }
+  if (t == 0) num_splits[batch] = used;
+  for (int p = used + t; p < num_parts; p += kSchedThreads) {
+    int32_t* m = meta + (int64_t)p * 8;
+    m[0] = m[1] = m[2] = m[3] = m[4] = -1;
+    m[5] = m[6] = m[7] = 0;
+  }
+  return true;
+}
+
+template <bool LOCAL>
 __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const int32_t* __restrict__ lengths, int batch,
                                                               int num_parts, int32_t* __restrict__ meta,
                                                               int32_t* __restrict__ num_splits) {
@@ -275,6 +362,16 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const int32_t* __r
   __shared__ int32_t wsum[kSchedThreads / 64];
   const int t = threadIdx.x;
   const int C = (batch + kSchedThreads - 1) / kSchedThreads;  // <= 32 consecutive requests per thread
+
+  if constexpr (LOCAL) {
+    for (int k = 0; k < C; ++k) {
+      const int r = t * C + k;
+      if (r < batch) cum[r] = (max(lengths[r], 0) + kPage - 1) / kPage;  // blocks per request
+    }
+    __syncthreads();
+    if (request_local_partition(cum, batch, num_parts, meta, num_splits, wsum)) return;
+    __syncthreads();  // fall back to the global partition below (cum is rebuilt)
+  }
 
   // 1. blocks per request, exclusive prefix -> cum
   int local = 0;
@@ -1539,9 +1636,13 @@ __global__ __launch_bounds__(64) void patch_kernel(const uint8_t* __restrict__ k
 
 // ------------------------------------------------------------------ launchers
 hipError_t launch_sched(const int32_t* lengths, int batch, int num_parts, int32_t* meta, int32_t* num_splits,
-                        hipStream_t stream) {
-  hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kSchedThreads), 0, stream, lengths, batch, num_parts, meta,
-                     num_splits);
+                        hipStream_t stream, bool request_local) {
+  if (request_local)
+    hipLaunchKernelGGL(sched_kernel<true>, dim3(1), dim3(kSchedThreads), 0, stream, lengths, batch, num_parts, meta,
+                       num_splits);
+  else
+    hipLaunchKernelGGL(sched_kernel<false>, dim3(1), dim3(kSchedThreads), 0, stream, lengths, batch, num_parts, meta,
+                       num_splits);
   return hipGetLastError();
 }
 

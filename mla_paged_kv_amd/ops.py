@@ -35,6 +35,7 @@ KV_BF16_PAGED = 0
 KV_FP8_PACKED = 1
 KV_FP8_INDEXED = 2
 KV_FP16_PAGED = 3
+SCHED_AUTO, SCHED_GLOBAL, SCHED_REQUEST_LOCAL = 0, 1, 2
 D_QK, D_V, PAGE, REC_BYTES = 576, 512, 64, 656
 SCHED_META_INTS = 8
 
@@ -54,6 +55,7 @@ _SIGS = {
     "mla_pack_selected_kv": ([_P, _i64, _P, _P, _i32, _i32, _i32, _P, _sz, _P], _i32),
     "mla_patch_packed_kv": ([_P, _i64, _P, _P, _i32, _i32, _i32, _P, _i32, _P, _sz, _P], _i32),
     "mla_sparse_kv_format": ([_i32, _i32, _i32, _sz, _i32, _P], _i32),
+    "mla_get_packed_decode_metadata": ([_P, _i32, _i32, _i32, _i32, _i32, _i32, _P, _P, _P], _i32),
     "mla_read_device_errors": ([_P, _P], _i32),
 }
 for _name, (_args, _res) in _SIGS.items():
@@ -141,6 +143,21 @@ def mla_get_decode_metadata(seqlens, batch, s_q, h_q, h_kv, num_parts, sched_met
 
 def _act_dtype(kv_format):
     return torch.float16 if kv_format == KV_FP16_PAGED else torch.bfloat16
+
+
+def mla_get_packed_decode_metadata(topk_length, batch, s_q, h_q, topk_capacity, num_parts, policy=SCHED_AUTO,
+                                   sched_meta=None, num_splits=None, stream=None):
+    _need(topk_length, "topk_length", torch.int32, (batch,))
+    dev = topk_length.device
+    if sched_meta is None:
+        sched_meta = torch.empty((num_parts, SCHED_META_INTS), dtype=torch.int32, device=dev)
+    if num_splits is None:
+        num_splits = torch.empty((batch + 1,), dtype=torch.int32, device=dev)
+    _need(sched_meta, "sched_meta", torch.int32, (num_parts, SCHED_META_INTS))
+    _need(num_splits, "num_splits", torch.int32, (batch + 1,))
+    _check(_lib.mla_get_packed_decode_metadata(_ptr(topk_length), batch, s_q, h_q, topk_capacity, num_parts, policy,
+                                               _ptr(sched_meta), _ptr(num_splits), _stream(stream)))
+    return sched_meta, num_splits
 
 
 def mla_decode_fwd(q, kv, kv_format, block_table, seqlens, softmax_scale, causal, sched_meta, num_splits, out, lse,

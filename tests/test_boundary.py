@@ -195,6 +195,16 @@ def test_patch_fails_closed(kw, status):
     assert ops.mla_last_error_message()
 
 
+def test_packed_metadata_fails_closed():
+    f = lib.mla_get_packed_decode_metadata
+    assert f(NULL, 2, 1, 64, 2048, 8, 0, FAKE, FAKE, NULL) == ops.MLA_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 2, 1, 64, 2048, 0, 0, FAKE, FAKE, NULL) == ops.MLA_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 2, 1, 64, 2048, 8, 3, FAKE, FAKE, NULL) == ops.MLA_ERR_INVALID_ARGUMENT   # unknown policy
+    assert f(FAKE, 2, 1, 96, 2048, 8, 0, FAKE, FAKE, NULL) == ops.MLA_ERR_UNSUPPORTED        # h_q not 64/128
+    assert f(FAKE, 2, 1, 64, 100, 8, 0, FAKE, FAKE, NULL) == ops.MLA_ERR_UNSUPPORTED         # capacity
+    assert f(FAKE, 0, 1, 64, 2048, 8, 0, FAKE, FAKE, NULL) == ops.MLA_ERR_INVALID_ARGUMENT
+
+
 def test_binding_refuses_host_tensors():
     import torch
 

@@ -246,6 +246,67 @@ def test_combine_kernel_against_oracle_partials():
     G.compare("combine", out, lse, ref_o, ref_l)
 
 
+# ----------------------------------------------------------------------------- scheduler for the sparse paths
+
+SCHED_CASES = [
+    ([2048] * 8, 256), ([1536, 2048, 1700, 1600], 64), ([1, 64, 65, 0, 300], 4), ([0, 0], 3), ([10], 5),
+    ([2048, 4096, 3000, 100], 9), ([64] * 5, 5), ([128, 64], 2), ([4096], 256), ([700, 0, 2049], 7),
+    (list(np.random.default_rng(5).integers(0, 3000, size=40)), 128),
+    (list(np.random.default_rng(6).integers(0, 3000, size=3000)), 2048),
+    ([64, 64, 64], 2),                                                  # more requests than parts: global
+]
+
+
+@pytest.mark.parametrize("lengths,P", SCHED_CASES)
+def test_packed_metadata_bit_exact(lengths, P):
+    b = len(lengths)
+    tl = torch.tensor(np.asarray(lengths, np.int32), device="cuda:0")
+    glob = O.sched_partition(lengths, P)
+    loc = O.sched_partition_request_local(lengths, P) or glob
+    for policy, ref in ((ops.SCHED_GLOBAL, glob), (ops.SCHED_REQUEST_LOCAL, loc)):
+        meta, ns = ops.mla_get_packed_decode_metadata(tl, b, 1, 64, 64, P, policy=policy)
+        torch.cuda.synchronize()
+        assert np.array_equal(meta.cpu().numpy(), ref[0]), policy
+        assert np.array_equal(ns.cpu().numpy(), ref[1]), policy
+
+
+def test_packed_metadata_auto_policy():
+    """AUTO is the global partition (measured faster on this GPU at every shape)."""
+    lengths = [1536, 2048, 1700, 1600, 2048, 1800, 1900, 2000]
+    P = 64
+    loc = O.sched_partition_request_local(lengths, P)
+    glob = O.sched_partition(lengths, P)
+    assert not np.array_equal(loc[0], glob[0])
+    tl = torch.tensor(np.asarray(lengths, np.int32), device="cuda:0")
+    for s_q, h_q, ref in ((1, 64, glob), (2, 64, glob), (1, 128, glob), (4, 64, glob)):
+        meta, ns = ops.mla_get_packed_decode_metadata(tl, 8, s_q, h_q, 2048, P)
+        torch.cuda.synchronize()
+        assert np.array_equal(meta.cpu().numpy(), ref[0]) and np.array_equal(ns.cpu().numpy(), ref[1]), (s_q, h_q)
+
+
+@pytest.mark.parametrize("name,seed,b,h,cap,topk,ctx,s_q,parts", [
+    ("rl-c5like", 180, 8, 64, 2048, [1536, 2048, 1700, 1600, 2048, 1800, 1900, 2000], 32768, 1, 64),
+    ("rl-tails-sq2", 181, 3, 64, 192, [192, 65, 0], 4096, 2, 7),
+])
+def test_fp8_decode_with_request_local_metadata(name, seed, b, h, cap, topk, ctx, s_q, parts):
+    G.say(f"fp8 request-local {name}")
+    w = W.sparse_workload(name, seed, b, h, cap, topk, context=ctx, s_q=s_q)
+    t = G.dev_tensors(w)
+    ref = oracle_sparse(w)
+    meta, ns = ops.mla_get_packed_decode_metadata(t["seqlens"], b, s_q, h, cap, parts, policy=ops.SCHED_REQUEST_LOCAL)
+    ws_d = torch.empty((ops.mla_decode_workspace_size(b, s_q, h, parts),), dtype=torch.uint8, device="cuda:0")
+    packed = ops.mla_pack_selected_kv(t["kcache_rec"], t["indices"], t["seqlens"])
+    for fmt, kv, ix in ((ops.KV_FP8_PACKED, packed, None), (ops.KV_FP8_INDEXED, t["kcache_rec"], t["indices"])):
+        out = torch.empty((b, s_q, h, 512), dtype=torch.bfloat16, device="cuda:0")
+        lse = torch.empty((b, s_q, h), dtype=torch.float32, device="cuda:0")
+        ops.mla_decode_fwd(t["q"], kv, fmt, ix, t["seqlens"], w.scale, False, meta, ns, out, lse, ws_d,
+                           topk_capacity=cap)
+        ops.mla_combine(ns, ws_d, b, s_q, h, parts, out, lse)
+        torch.cuda.synchronize()
+        G.compare(f"{name}-{fmt}", out, lse, *ref)
+    assert ops.mla_read_device_errors() == 0
+
+
 # ----------------------------------------------------------------------------- FP8 pack + packed decode
 
 @pytest.mark.parametrize("case", [
