@@ -1420,6 +1420,392 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
   MLA_PROF_DUMP((blockIdx.y * gridDim.x + blockIdx.x) * 8 + wv)
 }
 
+// ------------------------------------------------------------------ FP8 decode, wave-specialised
+//
+// The sparse FP8 paths with the two-role structure of decode_ws_kernel, and no
+// widened copy of the tile: the raw 656-byte records stay in the ring and the
+// E4M3 bytes are converted to bf16 in registers on their way to the MFMAs
+// (exact: every E4M3 value is a bf16 value).
+//   * QK waves 0..3 (16 rows each): K fragments are 8 E4M3 bytes per lane
+//     (ds_read_b64, four v_cvt_scalef32_pk_bf16_fp8 with scale 1); the RoPE
+//     k-steps read bf16 directly.  The four 128-dim NoPE blocks and the RoPE
+//     part accumulate apart, and each key's fp32 block scales combine them at
+//     the end of the tile.  The softmax of tile t-1 runs between the k-steps of
+//     tile t; P(t-1) is written four times, multiplied by each key's scale of
+//     NoPE block b for the PV waves of block b.  They also stream the ring.
+//   * PV waves 4..7: wave 4+w owns output columns [128w, 128w+128) -- NoPE
+//     block w -- for all rows.  V^T fragments come from ds_read_b64_tr_b8 (in a
+//     16-lane group, lane j addresses key 8g + j/2 at byte 8 (j & 1) of the 16
+//     columns; lane i receives column i of keys 8g .. 8g+7), converted like K.
+// One barrier per tile; the ring holds 4 raw tiles (2 in flight), as in the
+// bf16 kernel.  64 rows per workgroup (h_q is 64 or 128 on these paths).
+constexpr int kF8OffP = kStages * kRawTileBytes;                         // 98304: P[2 parities][4 blocks]
+constexpr int kF8OffAlpha = kF8OffP + 2 * 4 * kPBufBytes;                // 147456
+constexpr int kF8OffFlag = kF8OffAlpha + 2 * kMaxRowsPerWG * 4;          // 147968
+constexpr int kF8OffL = kF8OffFlag + 64;                                 // 148032
+constexpr int kF8LdsBytes = kF8OffL + kMaxRowsPerWG * 4;                 // 148288
+static_assert(kF8LdsBytes <= 160 * 1024, "FP8 wave-specialised LDS budget");
+constexpr int kF8QkDepth = 3;  // raw K fragment ring depth
+
+// 8 E4M3 bytes (two dwords, byte k = element k) -> 8 bf16, exactly
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 raw) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+__device__ __forceinline__ u32x2 lds_read_b64(const LDS_AS uint8_t* p) {
+  return *reinterpret_cast<const LDS_AS u32x2*>(p);
+}
+
+__device__ __forceinline__ u32x2 lds_read_tr8(const LDS_AS uint8_t* p) {
+  typedef int i32x2_t __attribute__((ext_vector_type(2)));
+  const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      reinterpret_cast<LDS_AS i32x2_t*>(const_cast<LDS_AS uint8_t*>(p)));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+template <bool IDX>
+__global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs a) {
+  constexpr int RB = 4, MB = 64;
+  constexpr int LPW = IDX ? kIdxLoadsPerWave : kRawLoadsPerWave;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[kF8LdsBytes];
+  LDS_AS uint8_t* smem = (LDS_AS uint8_t*)(smem_raw);
+  LDS_AS float* alpha_s = reinterpret_cast<LDS_AS float*>(smem + kF8OffAlpha);  // [2][64]
+  LDS_AS uint8_t* flag_s = smem + kF8OffFlag;                                    // [2][4] bytes
+  LDS_AS float* l_s = reinterpret_cast<LDS_AS float*>(smem + kF8OffL);
+
+  const int tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool is_qk = wv < 4;
+  const int w = wv & 3;
+  const int l = tid & 63, g = l >> 4, li = l & 15;
+  const int part = blockIdx.x, rbk = blockIdx.y;
+  const int begin_req = ld_const(a.sched_meta, part * 8 + 0);
+  if (begin_req < 0) return;
+  const int begin_blk = ld_const(a.sched_meta, part * 8 + 1);
+  const int end_req = ld_const(a.sched_meta, part * 8 + 2);
+  const int end_blk = ld_const(a.sched_meta, part * 8 + 3);
+  const int begin_split = ld_const(a.sched_meta, part * 8 + 4);
+  if (begin_req >= a.batch || end_req >= a.batch || end_req < begin_req) {  // not a scheduler record
+    if (threadIdx.x == 0) atomicOr(&g_error_flags, kErrMeta);
+    return;
+  }
+
+  std::conditional_t<IDX, IndexedLoader, TileLoader<true>> loader;
+  loader.init(w, l);  // used by the QK waves
+  const int row_local = 16 * w + li;
+  // PV: lane j of 16-lane group g addresses key 8g + j/2, column half j & 1
+  const int tr8_key = 8 * g + (li >> 1);
+  const int tr8_col = 8 * (li & 1);
+
+  for (int r = begin_req; r <= end_req; ++r) {
+    int seqlen = ld_const(a.seqlens, r);
+    if (seqlen < 0 || seqlen > a.cap) {
+      if (tid == 0) atomicOr(&g_error_flags, kErrSeqlen);
+      seqlen = seqlen < 0 ? 0 : a.cap;
+    }
+    // the selected keys of query token s of request r are row r * s_q + s
+    const int lrow = r * a.s_q + (rbk * MB) / a.h_q;
+    if constexpr (IDX) loader.n = seqlen;
+    const int nblk = (seqlen + kPage - 1) / kPage;
+    const int blk0 = (r == begin_req) ? begin_blk : 0;
+    const int blk1 = (r == end_req) ? end_blk : nblk;
+    const int t0 = blk0 * kPage;
+    const int t1 = min(blk1 * kPage, seqlen);
+    const int ntile = t1 > t0 ? (t1 - t0 + kTK - 1) / kTK : 0;
+    const int split = (r == begin_req) ? begin_split : 0;
+    const int ns0 = ld_const(a.num_splits, r);
+    const int nsplit = ld_const(a.num_splits, r + 1) - ns0;
+    const int slot = ns0 + split;
+    if (nsplit > 1 && (slot < 0 || slot >= a.slots)) {
+      if (threadIdx.x == 0) atomicOr(&g_error_flags, kErrMeta);
+      continue;
+    }
+    const int rho = rbk * MB + row_local;
+    auto raw_slot = [&](int t) -> const LDS_AS uint8_t* { return smem + kOffRaw + (t & 3) * kRawTileBytes; };
+
+    if (is_qk) {
+      // ================================================================ QK waves
+      const bool live = rho < a.M;
+      bf16x8 qreg[18];
+      {
+        const uint16_t* qrow = a.q + ((int64_t)r * a.M + (live ? rho : 0)) * kDQK + 8 * g;
+#pragma unroll
+        for (int s = 0; s < 18; ++s) {
+          const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 32 * s);
+          qreg[s] = live ? v : bf16x8{};
+        }
+      }
+      const int lim = live ? t1 : 0;
+      float mrow = -INFINITY, lpart = 0.f;
+      float sx[8];  // scaled scores of the tile whose softmax runs next (keys 16kb + 4g + i)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sx[k] = -INFINITY;
+
+      // softmax of tile ts in steps (one dependency level per k-step of the next tile)
+      float mx = 0.f, ma = 0.f, mb = 0.f, alpha = 1.f, nmref = 0.f, pw = 0.f, psum = 0.f;
+      float pv[8];
+      bool upd = false;
+      auto softmax_step = [&](int step, int ts) {
+        switch (step) {
+          case 0: ma = fmaxf(fmaxf(sx[0], sx[1]), fmaxf(sx[2], sx[3])); break;
+          case 1: mb = fmaxf(fmaxf(sx[4], sx[5]), fmaxf(sx[6], sx[7])); break;
+          case 2: mx = fmaxf(ma, mb); break;
+          case 3: mx = rowmax16(mx); break;
+          case 4: mx = rowmax32(mx); break;
+          case 5: upd = mx > mrow + kRescaleThreshold; break;
+          case 6: {
+            const float mnew = upd ? mx : mrow;
+            pw = mrow - mnew;
+            mrow = mnew;
+            break;
+          }
+          case 7:
+            alpha = upd ? fast_exp2(pw) : 1.f;
+            nmref = (mrow == -INFINITY) ? 0.f : -mrow;
+            break;
+          case 8:
+#pragma unroll
+            for (int k = 0; k < 4; ++k) pv[k] = fast_exp2(sx[k] + nmref);
+            break;
+          case 9:
+#pragma unroll
+            for (int k = 4; k < 8; ++k) pv[k] = fast_exp2(sx[k] + nmref);
+            break;
+          case 10:
+            psum = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+            lpart = lpart * alpha + psum;
+            break;
+          case 11:
+          case 12:
+          case 13:
+          case 14: {
+            // P of NoPE block b = step - 11: p times each key's scale b
+            const int b = step - 11;
+            const LDS_AS uint8_t* rawt = raw_slot(ts);
+            const int nvalid = min(kTK, t1 - (t0 + ts * kTK));
+            float sc[8];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int kr = 16 * kb + 4 * g + i;
+                sc[kb * 4 + i] = kr < nvalid ? *reinterpret_cast<const LDS_AS float*>(rawt + kr * kRecBytes + 512 + 4 * b)
+                                             : 0.f;
+              }
+            LDS_AS uint8_t* prow = smem + kF8OffP + ((ts & 1) * 4 + b) * kPBufBytes + row_local * kPStride + 8 * g;
+            *reinterpret_cast<LDS_AS u32x2*>(prow) =
+                u32x2{pack_bf16x2(pv[0] * sc[0], pv[1] * sc[1]), pack_bf16x2(pv[2] * sc[2], pv[3] * sc[3])};
+            *reinterpret_cast<LDS_AS u32x2*>(prow + 32) =
+                u32x2{pack_bf16x2(pv[4] * sc[4], pv[5] * sc[5]), pack_bf16x2(pv[6] * sc[6], pv[7] * sc[7])};
+            break;
+          }
+          case 15: {
+            const bool any = __any(upd);
+            if (any && g == 0) alpha_s[(ts & 1) * kMaxRowsPerWG + row_local] = alpha;
+            if (l == 0) flag_s[(ts & 1) * 4 + w] = any ? 1 : 0;
+            break;
+          }
+          default: break;
+        }
+      };
+
+      // QK^T of tile t (raw slot), scores combined with the block scales -> sx
+      auto qk = [&](int t, auto hook) {
+        const LDS_AS uint8_t* rawt = raw_slot(t);
+        const LDS_AS uint8_t* kr0p = rawt + li * kRecBytes + 8 * g;         // keys li (kb 0)
+        const LDS_AS uint8_t* kr1p = rawt + (16 + li) * kRecBytes + 8 * g;  // keys 16 + li (kb 1)
+        f32x4 acc[2][5];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int gi = 0; gi < 5; ++gi) acc[kb][gi] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // operand of k-step s: NoPE (s < 16) 8 E4M3 bytes at 32s, RoPE 16 B of bf16
+        auto opnd = [&](const LDS_AS uint8_t* p, int s) -> bf16x8 {
+          if (s < 16) return e4m3x8_to_bf16(lds_read_b64(p + 32 * s));
+          return lds_read_b128(p - 8 * g + 528 + 64 * (s - 16) + 16 * g);
+        };
+        u32x2 rk0[kF8QkDepth], rk1[kF8QkDepth];
+        bf16x8 rp0[2], rp1[2];
+#pragma unroll
+        for (int s = 0; s < kF8QkDepth - 1; ++s) {
+          rk0[s] = lds_read_b64(kr0p + 32 * s);
+          rk1[s] = lds_read_b64(kr1p + 32 * s);
+        }
+#pragma unroll
+        for (int s = 0; s < 18; ++s) {
+          const int sn = s + kF8QkDepth - 1;
+          if (sn < 16) {
+            rk0[sn % kF8QkDepth] = lds_read_b64(kr0p + 32 * sn);
+            rk1[sn % kF8QkDepth] = lds_read_b64(kr1p + 32 * sn);
+          } else if (sn < 18) {
+            rp0[sn - 16] = opnd(kr0p, sn);
+            rp1[sn - 16] = opnd(kr1p, sn);
+          }
+          const int gi = s < 16 ? (s >> 2) : 4;
+          const bf16x8 k0 = s < 16 ? e4m3x8_to_bf16(rk0[s % kF8QkDepth]) : rp0[s - 16];
+          const bf16x8 k1 = s < 16 ? e4m3x8_to_bf16(rk1[s % kF8QkDepth]) : rp1[s - 16];
+          acc[0][gi] = mfma16(k0, qreg[s], acc[0][gi]);
+          acc[1][gi] = mfma16(k1, qreg[s], acc[1][gi]);
+          hook(s);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // scores: RoPE part + sum over NoPE blocks of scale_b * block sum, masked
+        const int key0 = t0 + t * kTK;
+        const int nvalid = min(kTK, t1 - key0);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kr = 16 * kb + 4 * g + i;
+            const f32x4 sc = kr < nvalid ? *reinterpret_cast<const LDS_AS f32x4*>(rawt + kr * kRecBytes + 512)
+                                         : f32x4{0.f, 0.f, 0.f, 0.f};
+            float x = acc[kb][4][i] + sc[0] * acc[kb][0][i] + sc[1] * acc[kb][1][i] + sc[2] * acc[kb][2][i] +
+                      sc[3] * acc[kb][3][i];
+            x *= a.scale_log2;
+            sx[kb * 4 + i] = key0 + kr < lim ? x : -INFINITY;
+          }
+      };
+
+      if (ntile > 0) loader.issue(a, lrow, t0, smem, 0, w);
+      if (ntile > 1) loader.issue(a, lrow, t0 + kTK, smem, 1, w);
+      if (ntile > 1) wait_vmcnt<LPW>();
+      else wait_vmcnt<0>();
+      sync_lds();  // tile 0 resident
+      auto iter = [&](auto do_qk_c, auto do_sm_c, int t) {
+        constexpr bool DO_QK = decltype(do_qk_c)::value;
+        constexpr bool DO_SM = decltype(do_sm_c)::value;
+        const bool more = t + 2 < ntile;
+        if (more) loader.issue(a, lrow, t0 + (t + 2) * kTK, smem, (t + 2) & 3, w);
+        if constexpr (DO_QK) {
+          if constexpr (DO_SM) {
+            // the softmax of t-1 reads sx, which qk(t) overwrites only at its end
+            qk(t, [&](int s) { softmax_step(s, t - 1); });
+          } else {
+            qk(t, [](int) {});
+          }
+        } else if constexpr (DO_SM) {
+#pragma unroll
+          for (int step = 0; step < 16; ++step) softmax_step(step, t - 1);
+        }
+        if (t == ntile) {  // every tile's softmax is done: row sums for the output stage
+          const float lt = row4_sum(lpart);
+          if (g == 0) {
+            l_s[row_local] = lt;
+            if (rho < a.M) {
+              const float lse = lt > 0.f ? (mrow + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
+              if (nsplit == 1) a.lse[(int64_t)r * a.M + rho] = lse;
+              else a.part_lse[(int64_t)slot * a.M + rho] = lse;
+            }
+          }
+        }
+        if (t + 1 < ntile) {
+          if (more) wait_vmcnt<LPW>();
+          else wait_vmcnt<0>();
+        }
+        sync_lds();
+      };
+      using F = std::false_type;
+      using T = std::true_type;
+      if (ntile >= 1) {
+        iter(T{}, F{}, 0);
+        for (int t = 1; t < ntile; ++t) iter(T{}, T{}, t);
+        iter(F{}, T{}, ntile);
+      } else {
+        iter(F{}, F{}, 0);
+      }
+      iter(F{}, F{}, ntile + 1);
+    } else {
+      // ================================================================ PV waves
+      f32x4 o[8][RB];
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      u32x2 v[8];  // raw V^T fragments of one tile (this wave's 128 columns, 32 keys)
+      auto vread = [&](int t, int db) {
+        v[db] = lds_read_tr8(raw_slot(t) + tr8_key * kRecBytes + 128 * w + 16 * db + tr8_col);
+      };
+      sync_lds();  // tile 0 resident
+      auto iter = [&](auto do_pv_c, auto do_vread_c, int t) {
+        constexpr bool DO_PV = decltype(do_pv_c)::value;
+        constexpr bool DO_VREAD = decltype(do_vread_c)::value;
+        const int tp = t - 2;
+        uint32_t fl = 0;
+        float al[RB];
+        bf16x8 bp[RB];
+        if constexpr (DO_PV) {
+          const LDS_AS uint8_t* pb = smem + kF8OffP + ((tp & 1) * 4 + w) * kPBufBytes;
+          fl = *reinterpret_cast<const LDS_AS uint32_t*>(flag_s + (tp & 1) * 4);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) al[rb] = alpha_s[(tp & 1) * kMaxRowsPerWG + 16 * rb + li];
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) bp[rb] = lds_read_b128(pb + (16 * rb + li) * kPStride + 16 * g);
+          if (tp > 0) {
+            const uint32_t fls = __builtin_amdgcn_readfirstlane(fl);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+              if ((fls >> (8 * rb)) & 0xffu) {
+#pragma unroll
+                for (int db = 0; db < 8; ++db) o[db][rb] *= al[rb];
+              }
+            }
+          }
+#pragma unroll
+          for (int db = 0; db < 8; ++db) {
+            const bf16x8 av = e4m3x8_to_bf16(v[db]);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) o[db][rb] = mfma16(av, bp[rb], o[db][rb]);
+            if constexpr (DO_VREAD) vread(t - 1, db);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else if constexpr (DO_VREAD) {
+#pragma unroll
+          for (int db = 0; db < 8; ++db) vread(t - 1, db);
+        }
+        sync_lds();
+      };
+      using F = std::false_type;
+      using T = std::true_type;
+      iter(F{}, F{}, 0);
+      if (ntile >= 1) {
+        iter(F{}, T{}, 1);
+        for (int t = 2; t <= ntile; ++t) iter(T{}, T{}, t);
+        iter(T{}, F{}, ntile + 1);
+      } else {
+        iter(F{}, F{}, 1);
+      }
+      sync_lds();  // l from the QK waves (written in iteration ntile)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int rho_o = rbk * MB + 16 * rb + li;
+        if (rho_o >= a.M) continue;
+        const float lt = l_s[16 * rb + li];
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        if (nsplit == 1) {
+          uint16_t* orow = a.out + ((int64_t)r * a.M + rho_o) * kDV + 128 * w + 4 * g;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) {
+            const f32x4 vv = o[db][rb] * inv;
+            *reinterpret_cast<u32x2*>(orow + 16 * db) = u32x2{pack_bf16x2(vv[0], vv[1]), pack_bf16x2(vv[2], vv[3])};
+          }
+        } else {
+          float* prow = a.part_o + ((int64_t)slot * a.M + rho_o) * kDV + 128 * w + 4 * g;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(prow + 16 * db) = o[db][rb] * inv;
+        }
+      }
+      wait_vmcnt<0>();
+    }
+    if (is_qk) sync_lds();  // matches the PV waves' extra barrier before the output stage
+    sync_lds();             // every LDS buffer is reused by the next request of this partition
+  }
+}
+
 // 16-row blocks per workgroup.  Capped at 4 (64 rows): at 128 rows the Q and O
 // register tiles alone take ~400 of a wave's 512 registers and the compiler
 // spills; an h_q = 128 request is covered by two 64-row workgroups whose
@@ -1436,10 +1822,12 @@ static hipError_t launch_decode_t(const DecodeArgs& a, int kind, hipStream_t str
   const int MB = 16 * RB;
   const bool mkv = a.h_kv > 1;
   dim3 grid(a.num_parts, mkv ? a.h_kv * ((a.Mkv + MB - 1) / MB) : (a.M + MB - 1) / MB);
+  if ((kind == kDecodeFp8Packed || kind == kDecodeFp8Indexed) && RB != 4)
+    return hipErrorInvalidValue;  // the FP8 kernel covers 64 rows (h_q is 64 or 128 there)
   if (kind == kDecodeFp8Packed)
-    hipLaunchKernelGGL((decode_kernel<RB, true, false>), grid, dim3(kDecodeThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_fp8ws_kernel<false>), grid, dim3(kWsThreads), 0, stream, a);
   else if (kind == kDecodeFp8Indexed)
-    hipLaunchKernelGGL((decode_kernel<RB, true, true>), grid, dim3(kDecodeThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_fp8ws_kernel<true>), grid, dim3(kWsThreads), 0, stream, a);
   else if (kind == kDecodeF16 && mkv)
     hipLaunchKernelGGL((decode_ws_kernel<RB, true, true>), grid, dim3(kWsThreads), 0, stream, a);
   else if (kind == kDecodeF16)
@@ -1462,9 +1850,9 @@ hipError_t launch_decode(const DecodeArgs& a, int kind, hipStream_t stream) {
 template <int RB>
 static hipError_t occupancy_t(int kind, int* n) {
   if (kind == kDecodeFp8Packed)
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_kernel<RB, true, false>, kDecodeThreads, 0);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_fp8ws_kernel<false>, kWsThreads, 0);
   if (kind == kDecodeFp8Indexed)
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_kernel<RB, true, true>, kDecodeThreads, 0);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_fp8ws_kernel<true>, kWsThreads, 0);
   // (the several-KV-head instantiations use the same registers and LDS)
   if (kind == kDecodeF16)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_ws_kernel<RB, true, false>, kWsThreads, 0);
