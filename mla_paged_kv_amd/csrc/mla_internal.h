@@ -13,7 +13,6 @@ constexpr int kDV = 512;
 constexpr int kPage = 64;
 constexpr int kRecBytes = 656;
 constexpr int kMaxRowsPerWG = 64;   // query rows (token, head) one decode workgroup covers
-constexpr int kDecodeThreads = 256; // 4 waves of 64
 constexpr int kSchedMaxBatch = 8192;
 
 // Device-side violation flags (see mla_read_device_errors).

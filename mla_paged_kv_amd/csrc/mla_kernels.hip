@@ -9,26 +9,24 @@
 // splits merged by a log-sum-exp combine.
 //
 // gfx950 design (not the pages' SM80/SM90 tiling):
-//   * One workgroup = 4 waves (one per SIMD) = up to 128 query rows of one
-//     partition.  Every 32-key tile is fetched from HBM once per workgroup and
-//     serves all rows, which is what makes QK^T and PV dense contractions.
-//   * K/V tiles (32 keys x 1152 B) stream HBM -> LDS with global_load_lds
-//     (16 B per lane, no VGPR staging) through a 4-stage ring; 16-B chunks of a
-//     key row are XOR-swizzled by (row & 7), which keeps the 16-rows-per-read
-//     MFMA operand fetches free of bank conflicts despite the 1152-B row pitch.
-//   * QK^T as S^T = K Q^T with v_mfma_f32_16x16x32_bf16: K is the A operand
-//     (ds_read_b128 from LDS), Q the B operand held in registers for the whole
-//     split (wave w owns rows [16w, 16w+16) and [16(w+4), ...)).
-//   * PV as O^T = V^T P^T: V^T comes from the same LDS tile through
-//     ds_read_b64_tr_b16 transposed reads, P^T (bf16) from a small LDS buffer;
-//     wave w owns output columns [128w, 128w+128) for all rows, so P is
-//     computed once per row and shared, and each V element is read once.
+//   * One workgroup = 8 waves, two per SIMD with different jobs, covering up
+//     to 64 query rows of one partition: four QK waves (16 rows each, Q in
+//     registers) compute scores and the online softmax, four PV waves own 128
+//     output columns each for all rows.  Every 32-key tile is fetched once per
+//     workgroup and serves all its rows.
+//   * Tiles stream HBM -> LDS with global_load_lds (16 B per lane, no VGPR
+//     staging) through a 4-slot ring; bf16 key rows are stored with their 16-B
+//     chunks XOR-swizzled by (row & 7), which keeps the 16-rows-per-read MFMA
+//     operand fetches free of bank conflicts despite the 1152-B row pitch.
+//   * QK^T as S^T = K Q^T with v_mfma_f32_16x16x32 (K the A operand from LDS);
+//     PV as O^T = V^T P^T with V^T from transposed LDS reads and P^T (bf16)
+//     shared through LDS, so each score row is computed once.
 //   * Online softmax in the exp2 domain with lazy rescaling: the running max
 //     moves (and O is rescaled) only when a tile's max exceeds it by more than
 //     kRescaleThreshold (log2 units); final out = O / l is exact either way.
-//   * The FP8 packed variant loads 656-byte records into a raw LDS ring and
-//     dequantises each tile (E4M3 x fp32 scale -> bf16; RoPE copied) into the
-//     same swizzled bf16 tile the dense path uses.
+//   * The FP8 paths keep the raw 656-byte records in the ring and convert the
+//     E4M3 bytes to bf16 in registers on their way to the MFMAs (exact); each
+//     key's fp32 block scales multiply the per-block score sums and P.
 #include "mla_internal.h"
 
 #include <type_traits>
@@ -96,16 +94,6 @@ constexpr float kRescaleThreshold = 8.0f;           // log2 units: p <= 2^8 betw
 constexpr int kPBufBytes = kMaxRowsPerWG * kPStride;            // one P buffer (6 KB)
 constexpr int kOffKDense = 0;
 constexpr int kOffRaw = 0;                                      // FP8: raw ring
-constexpr int kOffKFp8 = kStages * kRawTileBytes;               // FP8: widened bf16 tile
-constexpr int kOffPDense = kStages * kTileBytes;                // 147456
-constexpr int kOffPFp8 = kOffKFp8 + kTileBytes;                 // 135168
-__host__ __device__ constexpr int off_p(bool fp8) { return fp8 ? kOffPFp8 : kOffPDense; }
-__host__ __device__ constexpr int off_alpha(bool fp8) { return off_p(fp8) + (fp8 ? 4 : 1) * kPBufBytes; }
-__host__ __device__ constexpr int off_flag(bool fp8) { return off_alpha(fp8) + kMaxRowsPerWG * 4; }
-__host__ __device__ constexpr int off_l(bool fp8) { return off_flag(fp8) + 64; }
-__host__ __device__ constexpr int lds_bytes(bool fp8) { return off_l(fp8) + kMaxRowsPerWG * 4; }
-static_assert(lds_bytes(false) <= 160 * 1024, "dense LDS budget");
-static_assert(lds_bytes(true) <= 160 * 1024, "fp8 LDS budget");
 
 // ------------------------------------------------------------------ small device helpers
 template <int N>
@@ -165,9 +153,6 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
-}
 
 // A score row lives in lanes l, l^16, l^32, l^48.  v_permlane16_swap /
 // v_permlane32_swap exchange half-rows between two registers; with both holding
@@ -193,15 +178,6 @@ __device__ __forceinline__ float rowmax32(float v) {
   float b = v;
   asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\tv_max_f32 %0, %0, %1" : "+v"(v), "+v"(b));
   return v;
-}
-__device__ __forceinline__ float row4_max(float v) {
-  float a = v, b = v;
-  permlane_pair16(a, b);
-  v = fmaxf(a, b);
-  a = v;
-  b = v;
-  permlane_pair32(a, b);
-  return fmaxf(a, b);
 }
 __device__ __forceinline__ float row4_sum(float v) {
   float a = v, b = v;
@@ -585,45 +561,6 @@ struct IndexedLoader {
   }
 };
 
-// Widen a raw FP8 tile into the swizzled bf16 tile: NoPE bytes E4M3 -> bf16 (exact:
-// every E4M3 value is a bf16 value; the per-block fp32 scales are applied later,
-// in fp32, to the scores and to P), RoPE copied.  Rows >= nvalid become zero.
-__device__ __forceinline__ void widen_fp8_tile(const LDS_AS uint8_t* raw, LDS_AS uint8_t* kt, int nvalid) {
-  for (int idx = threadIdx.x; idx < kTK * kChunksPerRow; idx += kDecodeThreads) {
-    const int kr = idx / kChunksPerRow;
-    const int c = idx - kr * kChunksPerRow;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (kr < nvalid) {
-      const LDS_AS uint8_t* rec = raw + kr * kRecBytes;
-      if (c < 64) {
-        const u32x2 codes = *reinterpret_cast<const LDS_AS u32x2*>(rec + c * 8);
-        const f32x2 f0 = __builtin_amdgcn_cvt_pk_f32_fp8(codes.x, false);
-        const f32x2 f1 = __builtin_amdgcn_cvt_pk_f32_fp8(codes.x, true);
-        const f32x2 f2 = __builtin_amdgcn_cvt_pk_f32_fp8(codes.y, false);
-        const f32x2 f3 = __builtin_amdgcn_cvt_pk_f32_fp8(codes.y, true);
-        v = u32x4{(uint32_t)f32_to_bf16_rne(f0.x) | ((uint32_t)f32_to_bf16_rne(f0.y) << 16),
-                  (uint32_t)f32_to_bf16_rne(f1.x) | ((uint32_t)f32_to_bf16_rne(f1.y) << 16),
-                  (uint32_t)f32_to_bf16_rne(f2.x) | ((uint32_t)f32_to_bf16_rne(f2.y) << 16),
-                  (uint32_t)f32_to_bf16_rne(f3.x) | ((uint32_t)f32_to_bf16_rne(f3.y) << 16)};
-      } else {
-        v = *reinterpret_cast<const LDS_AS u32x4*>(rec + 528 + (c - 64) * 16);
-      }
-    }
-    *reinterpret_cast<LDS_AS u32x4*>(kt + tile_off(kr, c)) = v;
-  }
-}
-
-// Zero V rows [nvalid, 32) of a bf16 tile (keys past the end of the sequence may
-// hold anything, and 0 * NaN would poison PV).
-__device__ __forceinline__ void zero_tail_rows(LDS_AS uint8_t* kt, int nvalid) {
-  const int n = (kTK - nvalid) * 64;  // 16-B chunks of the 512 V dims
-  for (int idx = threadIdx.x; idx < n; idx += kDecodeThreads) {
-    int kr = nvalid + (idx >> 6);
-    int c = idx & 63;
-    *reinterpret_cast<LDS_AS u32x4*>(kt + tile_off(kr, c)) = u32x4{0u, 0u, 0u, 0u};
-  }
-}
-
 // one v_cvt_pk_bf16_f32 (round to nearest even), a in the low half
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -651,289 +588,6 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), f16x2));
   else
     return pack_bf16x2(a, b);
-}
-
-// One workgroup: the 16*RB query rows of row block blockIdx.y, over the KV range
-// of partition blockIdx.x.  Wave w computes scores for rows [16w, 16w+16) (if
-// w < RB) and accumulates output columns [128w, 128w+128) for all rows.
-template <int RB, bool FP8, bool IDX = false>
-__global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(DecodeArgs a) {
-  static_assert(FP8 || !IDX, "indexed gather is an FP8 mode");
-  constexpr int MB = 16 * RB;  // rows per workgroup
-  static_assert(MB <= kMaxRowsPerWG, "row block");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[lds_bytes(FP8)];
-  LDS_AS uint8_t* smem = (LDS_AS uint8_t*)(smem_raw);  // C-style: generic -> LDS address space
-  LDS_AS uint8_t* pbuf = smem + off_p(FP8);
-  LDS_AS float* alpha_s = reinterpret_cast<LDS_AS float*>(smem + off_alpha(FP8));
-  LDS_AS int* flag_s = reinterpret_cast<LDS_AS int*>(smem + off_flag(FP8));
-  LDS_AS float* l_s = reinterpret_cast<LDS_AS float*>(smem + off_l(FP8));
-
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l = tid & 63, g = l >> 4, li = l & 15;
-  const bool qk_wave = w < RB;
-  const int part = blockIdx.x, rbk = blockIdx.y;
-  const int begin_req = ld_const(a.sched_meta, part * 8 + 0);
-  if (begin_req < 0) return;
-  const int begin_blk = ld_const(a.sched_meta, part * 8 + 1);
-  const int end_req = ld_const(a.sched_meta, part * 8 + 2);
-  const int end_blk = ld_const(a.sched_meta, part * 8 + 3);
-  const int begin_split = ld_const(a.sched_meta, part * 8 + 4);
-  if (begin_req >= a.batch || end_req >= a.batch || end_req < begin_req) {  // not a scheduler record
-    if (threadIdx.x == 0) atomicOr(&g_error_flags, kErrMeta);
-    return;
-  }
-
-  std::conditional_t<IDX, IndexedLoader, TileLoader<FP8>> loader;
-  loader.init(w, l);
-
-  // QK^T: per-lane K-operand byte offsets for even/odd 32-dim k-steps (see tile_off):
-  // row li (+16 for the second key block), chunk 4s+g stored at (4s+g)^(li&7).
-  const int kx = li & 7;
-  const uint32_t kq_base0 = (uint32_t)(li * kRowBytes + 16 * (4 * (0 ^ (kx >> 2)) + (g ^ (kx & 3))));
-  const uint32_t kq_base1 = (uint32_t)(li * kRowBytes + 16 * (4 * (1 ^ (kx >> 2)) + (g ^ (kx & 3))));
-  // PV: transposed V reads; lane (4r + j) of group g addresses key 8g + r (+4), dims 4j.. of a 16-dim block
-  const int tr_r = li >> 2, tr_j = li & 3;
-  // this wave's P buffer: FP8 keeps one per 128-column scale block (P times that block's scale)
-  LDS_AS uint8_t* pmine = pbuf + (FP8 ? w * kPBufBytes : 0);
-  const int row_local = 16 * w + li;  // this lane's score row within the workgroup (if qk_wave)
-
-  for (int r = begin_req; r <= end_req; ++r) {
-    int seqlen = ld_const(a.seqlens, r);
-    if (seqlen < 0 || (!FP8 && seqlen > a.max_pages * kPage) || (FP8 && seqlen > a.cap)) {
-      if (tid == 0) atomicOr(&g_error_flags, kErrSeqlen);
-      seqlen = seqlen < 0 ? 0 : (FP8 ? a.cap : a.max_pages * kPage);
-    }
-    // FP8: the selected keys of query token s of request r are row r * s_q + s of
-    // the packed workspace (or of the id lists); all rows of this workgroup
-    // belong to one token, as 16 * RB divides h_q there
-    const int lrow = FP8 ? r * a.s_q + (rbk * MB) / a.h_q : r;
-    if constexpr (IDX) loader.n = seqlen;
-    const int nblk = (seqlen + kPage - 1) / kPage;
-    const int blk0 = (r == begin_req) ? begin_blk : 0;
-    const int blk1 = (r == end_req) ? end_blk : nblk;
-    const int t0 = blk0 * kPage;
-    const int t1 = min(blk1 * kPage, seqlen);
-    const int ntile = t1 > t0 ? (t1 - t0 + kTK - 1) / kTK : 0;
-    const int split = (r == begin_req) ? begin_split : 0;
-    const int ns0 = ld_const(a.num_splits, r);
-    const int nsplit = ld_const(a.num_splits, r + 1) - ns0;
-    const int slot = ns0 + split;
-    if (nsplit > 1 && (slot < 0 || slot >= a.slots)) {  // inconsistent metadata: skip, never write out of range
-      if (threadIdx.x == 0) atomicOr(&g_error_flags, kErrMeta);
-      continue;
-    }
-
-    // ---- Q rows (B operand of S^T = K Q^T), visible-key limit, softmax state
-    const int rho = rbk * MB + row_local;  // row within the request
-    const bool live = qk_wave && rho < a.M;
-    bf16x8 qreg[18];
-    {
-      const uint16_t* qrow = a.q + ((int64_t)r * a.M + (live ? rho : 0)) * kDQK + 8 * g;
-#pragma unroll
-      for (int s = 0; s < 18; ++s) {
-        const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 32 * s);
-        qreg[s] = live ? v : bf16x8{};
-      }
-    }
-    int lim = 0;
-    if (live) {
-      int nvis = seqlen;
-      if (a.causal) nvis = min(max(seqlen - a.s_q + rho / a.h_q + 1, 0), seqlen);
-      lim = min(t1, nvis);
-    }
-    float mrow = -INFINITY, lpart = 0.f;
-    f32x4 o[8][RB];
-#pragma unroll
-    for (int db = 0; db < 8; ++db)
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // ---- pipeline prologue: tiles 0 .. kStages-2
-#pragma unroll
-    for (int tt = 0; tt < kStages - 1; ++tt)
-      if (tt < ntile) loader.issue(a, lrow, t0 + tt * kTK, smem, tt, w);
-
-    for (int tile = 0; tile < ntile; ++tile) {
-      // own loads of this tile done (later tiles may stay in flight) ...
-      constexpr int LPW = IDX ? kIdxLoadsPerWave : (FP8 ? kRawLoadsPerWave : kLoadsPerWave);
-      if (tile + 2 < ntile) wait_vmcnt<2 * LPW>();
-      else if (tile + 1 < ntile) wait_vmcnt<LPW>();
-      else wait_vmcnt<0>();
-      // ... and everyone's, and every wave is past PV of the previous tile
-      sync_lds();
-      if (tile + kStages - 1 < ntile)
-        loader.issue(a, lrow, t0 + (tile + kStages - 1) * kTK, smem, (tile + kStages - 1) % kStages, w);
-
-      const int key0 = t0 + tile * kTK;
-      const int nvalid = min(kTK, t1 - key0);
-      LDS_AS uint8_t* kt;
-      const LDS_AS uint8_t* raw = nullptr;
-      if constexpr (FP8) {
-        raw = smem + kOffRaw + (tile % kStages) * kRawTileBytes;
-        kt = smem + kOffKFp8;
-        widen_fp8_tile(raw, kt, nvalid);
-        sync_lds();
-      } else {
-        kt = smem + kOffKDense + (tile % kStages) * kTileBytes;
-        if (nvalid < kTK) zero_tail_rows(kt, nvalid);
-      }
-
-      // ---- phase A: S^T = K Q^T for this wave's 16 rows, online softmax, P -> LDS
-      if (qk_wave) {
-        // FP8: the four 128-dim NoPE blocks and the RoPE part accumulate apart
-        // (groups 0..3, 4) so that each key's block scales multiply exact sums.
-        constexpr int NG = FP8 ? 5 : 1;
-        f32x4 acc[2][NG];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int gi = 0; gi < NG; ++gi) acc[kb][gi] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // software pipeline over the 18 k-steps: operands of step s+1 are in
-        // flight while step s multiplies; the scheduling barriers stop the
-        // compiler from hoisting all 36 LDS reads (and their registers) up front
-        bf16x8 cur0 = lds_read_b128(kt + kq_base0);
-        bf16x8 cur1 = lds_read_b128(kt + kq_base0 + 16 * kRowBytes);
-#pragma unroll
-        for (int s = 0; s < 18; ++s) {
-          bf16x8 nxt0 = cur0, nxt1 = cur1;
-          if (s + 1 < 18) {
-            const uint32_t nb = (((s + 1) & 1) ? kq_base1 : kq_base0) + ((s + 1) >> 1) * 128;
-            nxt0 = lds_read_b128(kt + nb);
-            nxt1 = lds_read_b128(kt + nb + 16 * kRowBytes);
-          }
-          const int gi = FP8 ? (s < 16 ? (s >> 2) : 4) : 0;
-          acc[0][gi] = mfma16(cur0, qreg[s], acc[0][gi]);
-          acc[1][gi] = mfma16(cur1, qreg[s], acc[1][gi]);
-          cur0 = nxt0;
-          cur1 = nxt1;
-          __builtin_amdgcn_sched_barrier(0);
-        }
-
-        // lane holds scores of row row_local for keys 16kb + 4g + i
-        float sv[8];
-        f32x4 ksc[8];  // FP8: the 4 block scales of each of those keys
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int kr = 16 * kb + 4 * g + i;
-            float x;
-            if constexpr (FP8) {
-              // keys past the valid prefix get scale 0 (their bytes are not guaranteed finite)
-              ksc[kb * 4 + i] = kr < nvalid ? *reinterpret_cast<const LDS_AS f32x4*>(raw + kr * kRecBytes + 512)
-                                            : f32x4{0.f, 0.f, 0.f, 0.f};
-              const f32x4 sc = ksc[kb * 4 + i];
-              x = acc[kb][NG - 1][i] + sc[0] * acc[kb][0][i] + sc[1] * acc[kb][1 % NG][i] +
-                  sc[2] * acc[kb][2 % NG][i] + sc[3] * acc[kb][3 % NG][i];
-            } else {
-              x = acc[kb][0][i];
-            }
-            x *= a.scale_log2;
-            sv[kb * 4 + i] = key0 + kr < lim ? x : -INFINITY;
-            mx = fmaxf(mx, sv[kb * 4 + i]);
-          }
-        mx = row4_max(mx);
-        const float mold = mrow;
-        const bool upd = mx > mold + kRescaleThreshold;
-        const float mnew = upd ? mx : mold;
-        const float alpha = upd ? fast_exp2(mold - mnew) : 1.f;
-        mrow = mnew;
-        const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-        float pv[8];
-        float psum = 0.f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          pv[k] = fast_exp2(sv[k] - mref);
-          psum += pv[k];
-        }
-        lpart = lpart * alpha + psum;
-        // P[row][key] (bf16): keys 4g..4g+3 at byte 8g, keys 16+4g.. at byte 32+8g
-        if constexpr (FP8) {
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            LDS_AS uint8_t* prow = pbuf + b * kPBufBytes + row_local * kPStride + 8 * g;
-            *reinterpret_cast<LDS_AS u32x2*>(prow) =
-                u32x2{pack_bf16x2(pv[0] * ksc[0][b], pv[1] * ksc[1][b]), pack_bf16x2(pv[2] * ksc[2][b], pv[3] * ksc[3][b])};
-            *reinterpret_cast<LDS_AS u32x2*>(prow + 32) =
-                u32x2{pack_bf16x2(pv[4] * ksc[4][b], pv[5] * ksc[5][b]), pack_bf16x2(pv[6] * ksc[6][b], pv[7] * ksc[7][b])};
-          }
-        } else {
-          LDS_AS uint8_t* prow = pbuf + row_local * kPStride + 8 * g;
-          *reinterpret_cast<LDS_AS u32x2*>(prow) = u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
-          *reinterpret_cast<LDS_AS u32x2*>(prow + 32) = u32x2{pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
-        }
-        if (g == 0) alpha_s[row_local] = alpha;
-        const bool any = __any(upd);
-        if (l == 0) flag_s[w] = any ? 1 : 0;
-      }
-      sync_lds();
-
-      // ---- phase B: O^T[cols of wave w] += V^T P^T for all rows
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        if (flag_s[rb]) {
-          const float al = alpha_s[16 * rb + li];
-#pragma unroll
-          for (int db = 0; db < 8; ++db) o[db][rb] *= al;
-        }
-      }
-      bf16x8 bp[RB];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) bp[rb] = lds_read_b128(pmine + (16 * rb + li) * kPStride + 16 * g);
-      const int kr0 = 8 * g + tr_r;
-      const uint32_t within = (tr_j & 1) * 8;
-      // V^T operand of dim block db (16 columns): keys 8g..8g+7 of column 128w+16db+li
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const int c = 16 * w + 2 * db + (tr_j >> 1);  // chunk holding dims 128w + 16db + 4j ..
-        const bf16x4 v0 = lds_read_tr16(kt + tile_off(kr0, c) + within);
-        const bf16x4 v1 = lds_read_tr16(kt + tile_off(kr0 + 4, c) + within);
-        const bf16x8 av = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) o[db][rb] = mfma16(av, bp[rb], o[db][rb]);
-      }
-    }
-
-    // ---- epilogue: row sums to LDS, then normalise and store
-    if (qk_wave) {
-      const float lt = row4_sum(lpart);
-      if (g == 0) {
-        l_s[row_local] = lt;
-        if (rho < a.M) {
-          const float lse = lt > 0.f ? (mrow + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
-          if (nsplit == 1) a.lse[(int64_t)r * a.M + rho] = lse;
-          else a.part_lse[(int64_t)slot * a.M + rho] = lse;
-        }
-      }
-    }
-    sync_lds();
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int rho_o = rbk * MB + 16 * rb + li;
-      if (rho_o >= a.M) continue;
-      const float lt = l_s[16 * rb + li];
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      if (nsplit == 1) {
-        uint16_t* orow = a.out + ((int64_t)r * a.M + rho_o) * kDV + 128 * w + 4 * g;
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          const f32x4 v = o[db][rb] * inv;
-          *reinterpret_cast<u32x2*>(orow + 16 * db) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        }
-      } else {
-        float* prow = a.part_o + ((int64_t)slot * a.M + rho_o) * kDV + 128 * w + 4 * g;
-#pragma unroll
-        for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(prow + 16 * db) = o[db][rb] * inv;
-      }
-    }
-    // the next request of this partition reuses every LDS buffer: all waves are
-    // past the last PV and the l reads once they pass this barrier; its first
-    // loads must not overtake this request's stores in the vmcnt count
-    wait_vmcnt<0>();
-    sync_lds();
-  }
 }
 
 // ------------------------------------------------------------------ dense decode: LDS layout
