@@ -250,7 +250,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "kernel": "decode_ws_kernel<4>",
+            "kernel": "decode_ws_kernel<4, false, false>",
             "algorithmic_bytes_per_launch": kv_bytes,
             "mfma_tflops": round(flops / dec_mean_s / 1e12, 2),
             "mfma_frac": round(flops / dec_mean_s / 1e12 / PEAK_BF16_TFLOPS, 4),
