@@ -453,13 +453,17 @@ struct TileLoader<false> {
     for (int k = 0; k < kLoadsPerWave; ++k) issue_one(src, smem, st, w, k);
   }
   // Wave-uniform base address of tile (page, key0) for issue_one, in SGPRs.
+  // The page id is made wave-uniform first, so that the bounds check (one
+  // unsigned 32-bit compare: a negative id wraps above any pool size) and the
+  // address arithmetic run on the scalar unit.
   __device__ uint64_t tile_src(const DecodeArgs& a, int64_t page, int key0) const {
-    if (page < 0 || page >= a.num_pages) {
+    uint32_t pg = (uint32_t)__builtin_amdgcn_readfirstlane((int)page);
+    const uint32_t np = a.num_pages < (int64_t)INT32_MAX ? (uint32_t)a.num_pages : (uint32_t)INT32_MAX;
+    if (pg >= np) {
       if ((threadIdx.x & 63) == 0) atomicOr(&g_error_flags, kErrPage);
-      page = 0;  // stay in bounds; the output of this request is undefined
+      pg = 0;  // stay in bounds; the output of this request is undefined
     }
-    // 32 x 32 -> 64-bit product: page < 2^31
-    const uint64_t off = (uint64_t)(uint32_t)page * (uint32_t)(kPage * kRowBytes) + (uint32_t)((key0 & 63) * kRowBytes);
+    const uint64_t off = (uint64_t)pg * (uint32_t)(kPage * kRowBytes) + (uint32_t)((key0 & 63) * kRowBytes);
     return uniform_u64((uint64_t)(uintptr_t)a.kv + off);
   }
   // The k-th of this wave's kLoadsPerWave loads of a tile.
@@ -624,23 +628,21 @@ __device__ __forceinline__ void qk_tile(const LDS_AS uint8_t* kt, uint32_t base0
     k0[s] = lds_read_b128(kt + addr(s));
     k1[s] = lds_read_b128(kt + addr(s) + 16 * kRowBytes);
   }
-  // four independent accumulation chains (key block x k-step parity): an MFMA
-  // then waits for the one issued two k-steps earlier, not one
-  f32x4 c[2][2];
-  c[0][0] = c[0][1] = c[1][0] = c[1][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // one accumulation chain per key block, kept in the caller's registers: the
+  // two chains alternate, and an MFMA whose accumulator comes from the MFMA
+  // before the previous one issues at the full rate (measured)
+  acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < 18; ++s) {
     if (s + D - 1 < 18) {
       k0[(s + D - 1) % D] = lds_read_b128(kt + addr(s + D - 1));
       k1[(s + D - 1) % D] = lds_read_b128(kt + addr(s + D - 1) + 16 * kRowBytes);
     }
-    c[0][s & 1] = mfma16t<F16>(k0[s % D], qreg[s], c[0][s & 1]);
-    c[1][s & 1] = mfma16t<F16>(k1[s % D], qreg[s], c[1][s & 1]);
+    acc[0] = mfma16t<F16>(k0[s % D], qreg[s], acc[0]);
+    acc[1] = mfma16t<F16>(k1[s % D], qreg[s], acc[1]);
     hook(s);
     __builtin_amdgcn_sched_barrier(0);
   }
-  acc[0] = c[0][0] + c[0][1];
-  acc[1] = c[1][0] + c[1][1];
 }
 
 // ------------------------------------------------------------------ dense decode, wave-specialised
@@ -795,7 +797,14 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
         lim = min(t1, nvis);
       }
       float mrow = -INFINITY, lpart = 0.f;
-      f32x4 sacc[2];  // raw scores of the tile whose softmax runs in the next iteration
+      int lim_min = live ? lim : INT32_MAX;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) lim_min = min(lim_min, __shfl_xor(lim_min, off, 64));
+      lim_min = __builtin_amdgcn_readfirstlane(lim_min);
+      // raw scores: tile t's in sacc[t & 1], so that the softmax of tile t-1 reads
+      // its scores in place while tile t's are computed (the loop below is
+      // unrolled by two to keep the parity a compile-time index)
+      f32x4 sacc[2][2];
 
       // Online softmax of tile ts from its raw scores `sc`, in 18 steps, one per
       // k-step of the next tile's QK^T: the waves issue in order, so a dependent
@@ -803,38 +812,35 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
       // the two MFMAs of that step cover its latency.  The scale c > 0 (checked at
       // the boundary) is applied as max(c s) = c max(s) and exp2(c s - m) =
       // exp2(fma(s, c, -m)), one op per score.
-      float x[8], pv[8], mx = 0.f, ma = 0.f, mb = 0.f, alpha = 1.f, nmref = 0.f, s01 = 0.f, s23 = 0.f,
+      float pv[8], mx = 0.f, ma = 0.f, mb = 0.f, alpha = 1.f, nmref = 0.f, s01 = 0.f, s23 = 0.f,
             s45 = 0.f, s67 = 0.f, pw = 0.f;
       uint32_t wp[4] = {0u, 0u, 0u, 0u};
       bool upd = false;
-      auto softmax_step = [&](int step, int ts, const f32x4 (&sc)[2]) {
+      auto softmax_step = [&](int step, int ts, f32x4 (&sc)[2]) {
+        // x(i): score i of this lane's eight (key block i / 4, key 4g + i % 4)
+        auto x = [&](int i) -> float { return sc[i >> 2][i & 3]; };
         switch (step) {
           case 0:
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = sc[0][i];
-            break;
           case 1:
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x[4 + i] = sc[1][i];
             break;
           case 2: {
             // keys past a row's visible range score -inf; skipped when every row
             // of the wave sees the whole tile
             const int key0 = t0 + ts * kTK;
-            if (!__all(!live || key0 + kTK <= lim)) {
+            if (key0 + kTK > lim_min) {
 #pragma unroll
               for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                  if (key0 + 16 * kb + 4 * g + i >= lim) x[kb * 4 + i] = -INFINITY;
+                  if (key0 + 16 * kb + 4 * g + i >= lim) sc[kb][i] = -INFINITY;
             }
             break;
           }
           case 3:
-            ma = fmaxf(fmaxf(x[0], x[1]), x[2]);
-            mb = fmaxf(fmaxf(x[3], x[4]), x[5]);
+            ma = fmaxf(fmaxf(x(0), x(1)), x(2));
+            mb = fmaxf(fmaxf(x(3), x(4)), x(5));
             break;
-          case 4: ma = fmaxf(fmaxf(x[6], x[7]), ma); break;
+          case 4: ma = fmaxf(fmaxf(x(6), x(7)), ma); break;
           case 5: mx = fmaxf(ma, mb); break;
           case 6: mx = rowmax16(mx); break;
           case 7: mx = rowmax32(mx); break;
@@ -852,11 +858,11 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
             break;
           case 12:
 #pragma unroll
-            for (int k = 0; k < 4; ++k) pv[k] = fast_exp2(__builtin_fmaf(x[k], a.scale_log2, nmref));
+            for (int k = 0; k < 4; ++k) pv[k] = fast_exp2(__builtin_fmaf(x(k), a.scale_log2, nmref));
             break;
           case 13:
 #pragma unroll
-            for (int k = 4; k < 8; ++k) pv[k] = fast_exp2(__builtin_fmaf(x[k], a.scale_log2, nmref));
+            for (int k = 4; k < 8; ++k) pv[k] = fast_exp2(__builtin_fmaf(x(k), a.scale_log2, nmref));
             break;
           case 14:
             s01 = pv[0] + pv[1];
@@ -903,32 +909,30 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
       sync_lds();  // tile 0 resident
       MLA_PROF_RESET
       // one iteration; DO_QK: S(t) = QK^T(t), DO_SM: softmax of S(t-1) (in the
-      // shadow of the MFMAs when both run).  Instantiated per stage combination.
-      auto iter = [&](auto do_qk_c, auto do_sm_c, int t) {
+      // shadow of the MFMAs when both run); PAR = t & 1.  Instantiated per stage
+      // combination and parity.
+      auto iter = [&](auto do_qk_c, auto do_sm_c, auto par_c, int t) {
         constexpr bool DO_QK = decltype(do_qk_c)::value;
         constexpr bool DO_SM = decltype(do_sm_c)::value;
+        constexpr int PAR = decltype(par_c)::value;
         // loads of tile t+2 into the slot of tile t-2 (its K was read in
         // iteration t-2, its V in iteration t-1)
         const bool more = t + 2 < ntile;
         if (more) issue_tile(uniform(pg_next), t0 + (t + 2) * kTK, (t + 2) & 3);
         if (has_rows) {
           if constexpr (DO_QK) {
-            f32x4 acc[2];
             const LDS_AS uint8_t* kt = smem + kOffKDense + (t & 3) * kTileBytes;
             if constexpr (DO_SM) {
-              const f32x4 prev[2] = {sacc[0], sacc[1]};
               // one softmax step after each k-step
-              qk_tile<kQkDepth, F16>(kt, kq_base0, kq_base1, qreg, acc, [&](int s) {
-                softmax_step(s, t - 1, prev);
+              qk_tile<kQkDepth, F16>(kt, kq_base0, kq_base1, qreg, sacc[PAR], [&](int s) {
+                softmax_step(s, t - 1, sacc[PAR ^ 1]);
               });
             } else {
-              qk_tile<kQkDepth, F16>(kt, kq_base0, kq_base1, qreg, acc);
+              qk_tile<kQkDepth, F16>(kt, kq_base0, kq_base1, qreg, sacc[PAR]);
             }
-            sacc[0] = acc[0];
-            sacc[1] = acc[1];
           } else if constexpr (DO_SM) {
 #pragma unroll
-            for (int step = 0; step < 18; ++step) softmax_step(step, t - 1, sacc);
+            for (int step = 0; step < 18; ++step) softmax_step(step, t - 1, sacc[PAR ^ 1]);
           }
           if (t == ntile) {  // every tile's softmax is done: row sums for the output stage
             const float lt = row4_sum(lpart);
@@ -954,16 +958,24 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
       };
       using F = std::false_type;
       using T = std::true_type;
+      using P0 = std::integral_constant<int, 0>;
+      using P1 = std::integral_constant<int, 1>;
       // t = 0: QK only; 1..ntile-1: QK + softmax(t-1); ntile: softmax only;
       // ntile+1: nothing (the PV waves drain)
       if (ntile >= 1) {
-        iter(T{}, F{}, 0);
-        for (int t = 1; t < ntile; ++t) iter(T{}, T{}, t);
-        iter(F{}, T{}, ntile);
+        iter(T{}, F{}, P0{}, 0);
+        int t = 1;
+        for (; t + 1 < ntile; t += 2) {
+          iter(T{}, T{}, P1{}, t);
+          iter(T{}, T{}, P0{}, t + 1);
+        }
+        if (t < ntile) iter(T{}, T{}, P1{}, t++);
+        if (t & 1) iter(F{}, T{}, P1{}, t);
+        else iter(F{}, T{}, P0{}, t);
       } else {
-        iter(F{}, F{}, 0);
+        iter(F{}, F{}, P0{}, 0);
       }
-      iter(F{}, F{}, ntile + 1);
+      iter(F{}, F{}, P0{}, ntile + 1);
       MLA_PROF_TILES(ntile)
     } else {
       // ================================================================ PV waves
@@ -972,12 +984,21 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
       for (int db = 0; db < 8; ++db)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      bf16x4 v[8][2];  // V^T fragments of one tile (this wave's 128 columns, 32 keys)
+      bf16x8 v8[8];  // V^T fragments of one tile (this wave's 128 columns, 32 keys)
+      // per-lane offsets of the transposed reads: column chunk c = 16w + 2db + (tr_j >> 1)
+      // swizzled with the key row; db and db + 4 differ by 8 chunks (bit 3, which
+      // the 3-bit swizzle leaves alone), i.e. by 128 bytes
+      uint32_t voff0[4], voff1[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int c = 16 * w + 2 * d + (tr_j >> 1);
+        voff0[d] = tile_off(kr0, c) + tr_within;
+        voff1[d] = tile_off(kr1, c) + tr_within;
+      }
       auto vread = [&](int t, int db) {
-        const LDS_AS uint8_t* kt = smem + kOffKDense + (t & 3) * kTileBytes;
-        const int c = 16 * w + 2 * db + (tr_j >> 1);
-        v[db][0] = lds_read_tr16(kt + tile_off(kr0, c) + tr_within);
-        v[db][1] = lds_read_tr16(kt + tile_off(kr1, c) + tr_within);
+        const LDS_AS uint8_t* kt = smem + kOffKDense + (t & 3) * kTileBytes + (db >> 2) * 128;
+        v8[db] = __builtin_shufflevector(lds_read_tr16(kt + voff0[db & 3]), lds_read_tr16(kt + voff1[db & 3]), 0, 1, 2, 3,
+                                         4, 5, 6, 7);
       };
 
       sync_lds();  // tile 0 resident
@@ -1019,7 +1040,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
           }
 #pragma unroll
           for (int db = 0; db < 8; ++db) {
-            const bf16x8 av = __builtin_shufflevector(v[db][0], v[db][1], 0, 1, 2, 3, 4, 5, 6, 7);
+            const bf16x8 av = v8[db];
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) o[db][rb] = mfma16t<F16>(av, bp[rb], o[db][rb]);
             if constexpr (DO_VREAD) vread(tv, db);
