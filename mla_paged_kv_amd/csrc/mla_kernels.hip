@@ -1565,9 +1565,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
     return;
   }
   uint16_t* orow = out + ((int64_t)r * M + rho) * kDV + 8 * l;
-  // the split lse values, 64 at a time, one per lane: max and sum by wave reductions
-  float mx = -INFINITY;
-  for (int i0 = 0; i0 < S; i0 += 64) {
+  const float* src0 = part_o + ((int64_t)s0 * M + rho) * kDV + 8 * l;
+  const int64_t stride = (int64_t)M * kDV;
+  // A split request has at least two pieces: the partial rows of the first two
+  // are loaded together with the lse values rather than after the reductions,
+  // which takes one dependent memory round trip off every wave.
+  f32x4 pa0 = {0.f, 0.f, 0.f, 0.f}, pb0 = pa0, pa1 = pa0, pb1 = pa0;
+  if (S >= 2) {
+    pa0 = *reinterpret_cast<const f32x4*>(src0);
+    pb0 = *reinterpret_cast<const f32x4*>(src0 + 4);
+    pa1 = *reinterpret_cast<const f32x4*>(src0 + stride);
+    pb1 = *reinterpret_cast<const f32x4*>(src0 + stride + 4);
+  }
+  // the split lse values, 64 at a time, one per lane: max and sum by wave
+  // reductions (the first 64 stay in v0)
+  const float v0 = l < S ? part_lse[(int64_t)(s0 + l) * M + rho] : -INFINITY;
+  float mx = v0;
+  for (int i0 = 64; i0 < S; i0 += 64) {
     const float v = i0 + l < S ? part_lse[(int64_t)(s0 + i0 + l) * M + rho] : -INFINITY;
     mx = fmaxf(mx, v);
   }
@@ -1578,20 +1592,27 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
     if (l == 0) lse[(int64_t)r * M + rho] = -INFINITY;
     return;
   }
-  float tot = 0.f;
-  for (int i0 = 0; i0 < S; i0 += 64) {
+  float tot = expf(v0 - mx);
+  for (int i0 = 64; i0 < S; i0 += 64) {
     const float v = i0 + l < S ? part_lse[(int64_t)(s0 + i0 + l) * M + rho] : -INFINITY;
     tot += expf(v - mx);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
   const float L = mx + logf(tot);
-  // weighted sum of the partial rows; lane l owns columns [8l, 8l+8).  Four
-  // splits per step so that their loads are in flight together.
+  // weighted sum of the partial rows in split order; lane l owns columns
+  // [8l, 8l+8).  After the first two, four splits per step so that their loads
+  // are in flight together.
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  const float* src0 = part_o + ((int64_t)s0 * M + rho) * kDV + 8 * l;
-  const int64_t stride = (int64_t)M * kDV;
   int i = 0;
+  if (S >= 2) {
+    const float w0 = expf(__shfl(v0, 0, 64) - L), w1 = expf(__shfl(v0, 1, 64) - L);
+    acc0 += w0 * pa0;
+    acc1 += w0 * pb0;
+    acc0 += w1 * pa1;
+    acc1 += w1 * pb1;
+    i = 2;
+  }
   for (; i + 4 <= S; i += 4) {
     f32x4 a[4], b[4];
     float wgt[4];
