@@ -940,8 +940,12 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
               l_s[row_local] = lt;
               if (rho < Mloc) {
                 const float lse = lt > 0.f ? (mrow + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
-                if (nsplit == 1) a.lse[(int64_t)r * a.M + grow(rho)] = lse;
-                else a.part_lse[(int64_t)slot * a.M + grow(rho)] = lse;
+                // row index made opaque here: otherwise the compiler hoists the
+                // 64-bit store addresses out of the request loop and spills them
+                int gr = grow(rho);
+                asm volatile("" : "+v"(gr));
+                if (nsplit == 1) a.lse[(int64_t)r * a.M + gr] = lse;
+                else a.part_lse[(int64_t)slot * a.M + gr] = lse;
               }
             }
           }
@@ -1070,7 +1074,8 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
       for (int rb = 0; rb < RB; ++rb) {
         const int rho_l = rbk * MB + 16 * rb + li;
         if (rho_l >= Mloc) continue;
-        const int rho_o = grow(rho_l);
+        int rho_o = grow(rho_l);
+        asm volatile("" : "+v"(rho_o));  // keeps the row addresses from being hoisted and spilled
         const float lt = l_s[16 * rb + li];
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         if (nsplit == 1) {
