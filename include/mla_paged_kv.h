@@ -125,8 +125,14 @@ size_t mla_decode_workspace_size(int batch, int s_q, int h_q, int num_parts);
  * row -- "Runtime follow-up", FlashMLA PR 200).  0 on bad input. */
 size_t mla_packed_kv_workspace_size(int batch, int s_q, int topk_capacity);
 
-/* Scheduler metadata (device, one workgroup).  Splits the KV blocks of all
- * requests into num_parts contiguous partitions.  Definition: request r has
+/* Scheduler metadata (device, one workgroup).  The dense page runs a
+ * scheduler-metadata kernel ahead of the decode (get_decoding_sched_meta,
+ * "Modifications outside csrc/sm80/", "Add SM80 (Ampere/A100) dense MLA decode
+ * kernel", FlashMLA PR 183) and scales the partition count to resident
+ * workgroups ("How the occupancy work went"); it does not spell out the
+ * partition rule, so the rule below is this library's reading.  Splits the KV
+ * blocks of all requests into num_parts contiguous partitions.  Definition:
+ * request r has
  * ceil(seqlens[r] / 64) blocks (seqlens = topk_length for the packed path),
  * T blocks in total, and P' = min(num_parts, T); concatenating all requests'
  * blocks in order, partition p < P' owns global blocks
@@ -144,7 +150,7 @@ int mla_get_decode_metadata(const int32_t* seqlens, int batch, int s_q, int h_q,
 
 /* Scheduler policies of mla_get_packed_decode_metadata. */
 typedef enum {
-  MLA_SCHED_AUTO = 0,          /* the hybrid policy described below */
+  MLA_SCHED_AUTO = 0,          /* = MLA_SCHED_GLOBAL on this GPU (measured; see below) */
   MLA_SCHED_GLOBAL = 1,        /* the partition of mla_get_decode_metadata */
   MLA_SCHED_REQUEST_LOCAL = 2  /* no partition spans two requests */
 } mla_sched_policy;
@@ -172,7 +178,14 @@ int mla_get_packed_decode_metadata(const int32_t* topk_length, int batch, int s_
                                    int num_parts, int policy, int32_t* sched_meta, int32_t* num_splits,
                                    void* stream);
 
-/* Decode (device).  Launches num_parts x h_kv * ceil(s_q*h_q/h_kv / R) workgroups
+/* Decode (device): the dense decode kernel of "Add SM80 (Ampere/A100) dense MLA
+ * decode kernel" (FlashMLA PR 183: Summary -- dense_decode_fwd plus the
+ * combine kernel; Design -- 576-dim Q/K shared by all heads, 512 V columns;
+ * Test plan -- BF16 and FP16, multi-KV-head, causal multi-token Q, split-K),
+ * and for the FP8 formats the packed attention specialization of "[SM90] Add
+ * packed selected-KV sparse decode" (FlashMLA PR 200: "Packed attention
+ * specialization", partial-tail masking).
+ * Launches num_parts x h_kv * ceil(s_q*h_q/h_kv / R) workgroups
  * (R = 16, 32 or 64 query rows of one KV head per workgroup); each walks its
  * partition's pages with an
  * online softmax and writes either the final out/lse rows (request not split)
@@ -215,7 +228,10 @@ int mla_decode_fwd(const void* q, const void* kv, int kv_format, int64_t num_pag
                    float softmax_scale, int causal, const int32_t* sched_meta, const int32_t* num_splits,
                    int num_parts, void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Combine (device): for every request with >= 2 splits, merges its partials
+/* Combine (device): the combine kernel that merges split-K partials ("Add
+ * SM80 (Ampere/A100) dense MLA decode kernel", FlashMLA PR 183: Summary, and
+ * "Modifications outside csrc/sm80/" on its split ladder; Test plan: split-K
+ * via the combine kernel).  For every request with >= 2 splits, merges its partials
  * from `workspace` by log-sum-exp, L = log(sum_i exp(lse_i)),
  * out = sum_i exp(lse_i - L) * o_i, lse = L (a split with lse -inf has weight
  * 0); a request with 0 splits (no key) gets out = 0, lse = -inf; a request with
@@ -226,7 +242,10 @@ int mla_decode_fwd(const void* q, const void* kv, int kv_format, int64_t num_pag
 int mla_combine(const int32_t* num_splits, const void* workspace, size_t workspace_bytes, int batch, int s_q,
                 int h_q, int num_parts, int kv_format, void* out, float* lse, void* stream);
 
-/* Pack (device): copies the selected 656-byte records byte-for-byte into the
+/* Pack (device): the packing kernel of "[SM90] Add packed selected-KV sparse
+ * decode" (FlashMLA PR 200, "SM90 packing kernel": selected 656-byte records
+ * copied byte for byte into a 64-token tile-major workspace, invalid suffix
+ * zero-filled).  Copies the selected 656-byte records byte-for-byte into the
  * tile-major workspace ws[row][tile][slot][656], row = r * s_q + i,
  * tile = k / 64, slot = k % 64, for k < topk_length[r] the record of physical
  * token indices[r][i][k] (page = id / 64, slot = id % 64); slots

@@ -160,22 +160,6 @@ int mla_get_decode_metadata(const int32_t* seqlens, int batch, int s_q, int h_q,
   return ok();
 }
 
-// Policy of the packed path (see mla_get_packed_decode_metadata).  The page
-// selects its request-local scheduler for H = 64 outside one fallback regime
-// on its GPU.  Measured here (HIP-graph step, metadata + packed decode +
-// combine, h_q 64 and 128, batch * s_q 1..32, full and uneven top-k 2048):
-// the global partition is 4-16 % faster at every shape -- with equal lengths
-// both give the same partition and the request-local search costs the
-// one-workgroup scheduler several microseconds -- so AUTO picks it everywhere.
-bool use_request_local(int batch, int s_q, int h_q, int topk_capacity, int num_parts) {
-  (void)batch;
-  (void)s_q;
-  (void)h_q;
-  (void)topk_capacity;
-  (void)num_parts;
-  return false;
-}
-
 int mla_get_packed_decode_metadata(const int32_t* topk_length, int batch, int s_q, int h_q, int topk_capacity,
                                    int num_parts, int policy, int32_t* sched_meta, int32_t* num_splits,
                                    void* stream) {
@@ -190,8 +174,13 @@ int mla_get_packed_decode_metadata(const int32_t* topk_length, int batch, int s_
     return fail(MLA_ERR_UNSUPPORTED, "topk_capacity %d must be a positive multiple of 64", topk_capacity);
   st = check_device();
   if (st) return st;
-  const bool local = policy == MLA_SCHED_REQUEST_LOCAL ||
-                     (policy == MLA_SCHED_AUTO && use_request_local(batch, s_q, h_q, topk_capacity, num_parts));
+  // AUTO is the global partition.  The page selects its request-local
+  // scheduler for H = 64 outside one fallback regime on its GPU; here (HIP-graph
+  // step, metadata + packed decode + combine, h_q 64 and 128, batch * s_q
+  // 1..32, full and uneven top-k 2048) the global partition measured 4-16 %
+  // faster at every shape: with equal lengths both give the same partition, and
+  // the request-local search costs the one-workgroup scheduler several us.
+  const bool local = policy == MLA_SCHED_REQUEST_LOCAL;
   hipError_t e = mla::launch_sched(topk_length, batch, num_parts, sched_meta, num_splits, (hipStream_t)stream, local);
   if (e != hipSuccess) return hip_fail(e, "scheduler launch");
   return ok();

@@ -45,24 +45,6 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ int g_error_flags;
 
-// Phase-timing hooks for the wave-specialised kernel.  They expand to nothing
-// unless MLA_PROFILE is defined (a profiling build reads the per-wave sums of
-// s_memtime deltas through mla_debug_read_prof).
-#ifdef MLA_PROFILE
-__device__ unsigned long long g_prof[4096 * 16];
-#define MLA_PROF_DECL unsigned long long prof_acc_[8] = {}, prof_tiles_ = 0; unsigned prof_last_ = (unsigned)__builtin_amdgcn_s_memtime();
-#define MLA_PROF_RESET prof_last_ = (unsigned)__builtin_amdgcn_s_memtime();
-#define MLA_PROF(i) do { unsigned c_ = (unsigned)__builtin_amdgcn_s_memtime(); prof_acc_[i] += (unsigned)(c_ - prof_last_); prof_last_ = c_; } while (0)
-#define MLA_PROF_TILES(n) prof_tiles_ += (n);
-#define MLA_PROF_DUMP(slot) if ((threadIdx.x & 63) == 0) { for (int i_ = 0; i_ < 8; ++i_) g_prof[(slot) * 16 + i_] = prof_acc_[i_]; g_prof[(slot) * 16 + 15] = prof_tiles_; }
-#else
-#define MLA_PROF_DECL
-#define MLA_PROF_RESET
-#define MLA_PROF(i)
-#define MLA_PROF_TILES(n)
-#define MLA_PROF_DUMP(slot)
-#endif
-
 // Read-only kernel inputs that every lane of a wave indexes the same way (page
 // table, lengths, scheduler records) are read through the constant address
 // space so that they become scalar loads: a vector load here would need a
@@ -113,10 +95,17 @@ __device__ __forceinline__ void sync_lds() {
 // Issued through inline asm on purpose: the compiler then knows of no pending
 // LDS DMA, so it inserts no vmcnt(0) in front of later LDS reads (it cannot
 // tell they touch other ring slots).  The ring's completion is tracked with the
-// explicit wait_vmcnt calls instead.  Nothing else in these kernels uses M0.
+// explicit wait_vmcnt calls instead.  M0 is a register the compiler reserves
+// (it cannot be listed as clobbered), so the asm saves and restores it; the
+// s_nop is the one wait state an SALU write of M0 needs before an LDS-DMA load.
 __device__ __forceinline__ void load_lds16(const void* gsrc, LDS_AS void* ldst) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)ldst);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(m0v) : "memory");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gsrc), "s"(m0v)
+      : "memory");
 }
 
 // Same, with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane offset
@@ -124,7 +113,12 @@ __device__ __forceinline__ void load_lds16(const void* gsrc, LDS_AS void* ldst) 
 // `bu` must be wave-uniform and already in SGPRs (see uniform_u64).
 __device__ __forceinline__ void load_lds16_s(uint64_t bu, uint32_t voff, LDS_AS void* ldst) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)ldst);
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(bu), "s"(m0v) : "memory");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(bu), "s"(m0v)
+      : "memory");
 }
 
 // A wave-uniform 64-bit value made visible as such (SGPRs).  The builtin returns
@@ -741,7 +735,6 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
   const int tr_j = li & 3;
   const uint32_t tr_within = (tr_j & 1) * 8;
   const int row_local = 16 * w + li;
-  MLA_PROF_DECL
 
   for (int r = begin_req; r <= end_req; ++r) {
     int seqlen = ld_const(a.seqlens, r);
@@ -907,7 +900,6 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
       if (ntile > 1) wait_vmcnt<kLPW>();
       else wait_vmcnt<0>();
       sync_lds();  // tile 0 resident
-      MLA_PROF_RESET
       // one iteration; DO_QK: S(t) = QK^T(t), DO_SM: softmax of S(t-1) (in the
       // shadow of the MFMAs when both run); PAR = t & 1.  Instantiated per stage
       // combination and parity.
@@ -949,7 +941,6 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
               }
             }
           }
-          MLA_PROF(0);
         }
         // own loads of tile t+1 done (tile t+2 may stay in flight)
         if (t + 1 < ntile) {
@@ -958,7 +949,6 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
         }
         if (t + 3 < ntile) pg_next = page_raw(t + 3);
         sync_lds();
-        MLA_PROF(2);
       };
       using F = std::false_type;
       using T = std::true_type;
@@ -980,7 +970,6 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
         iter(F{}, F{}, P0{}, 0);
       }
       iter(F{}, F{}, P0{}, ntile + 1);
-      MLA_PROF_TILES(ntile)
     } else {
       // ================================================================ PV waves
       f32x4 o[8][RB];
@@ -1006,7 +995,6 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
       };
 
       sync_lds();  // tile 0 resident
-      MLA_PROF_RESET
       // one iteration; DO_PV: PV(t-2) from registers, DO_VREAD: V(t-1) into
       // registers.  Instantiated per stage combination so that the steady-state
       // loop carries no stage conditions (and no register copies for them).
@@ -1030,7 +1018,6 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) bp[rb] = lds_read_b128(pb + (16 * rb + li) * kPStride + 16 * g);
         }
-        MLA_PROF(6);
         if constexpr (DO_PV) {
           if (tp > 0) {  // O is still zero before the first tile: nothing to rescale
             const uint32_t fls = __builtin_amdgcn_readfirstlane(fl);
@@ -1054,9 +1041,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
 #pragma unroll
           for (int db = 0; db < 8; ++db) vread(tv, db);
         }
-        MLA_PROF(3);
         sync_lds();
-        MLA_PROF(5);
       };
       using F = std::false_type;
       using T = std::true_type;
@@ -1068,7 +1053,6 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
       } else {
         iter(F{}, F{}, 1);
       }
-      MLA_PROF_TILES(ntile)
       sync_lds();  // l from the QK waves (written in iteration ntile)
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
@@ -1097,7 +1081,6 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
     // every LDS buffer is reused by the next request of this partition
     sync_lds();
   }
-  MLA_PROF_DUMP((blockIdx.y * gridDim.x + blockIdx.x) * 8 + wv)
 }
 
 // ------------------------------------------------------------------ FP8 decode, wave-specialised
@@ -1135,6 +1118,18 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 raw) {
   const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], 1.0f, false);
   const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], 1.0f, true);
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Zero the 512 NoPE bytes (the V part) of records [nvalid, 32) of a raw FP8
+// tile; `tid` in [0, 256) strides by 256.  Keys past the valid count score -inf
+// and get P = 0, but 0 * NaN would still poison PV if such a record's bytes
+// decode to NaN (the by-index loader reads record 0 for them).
+__device__ __forceinline__ void zero_tail_records_256(LDS_AS uint8_t* raw, int nvalid, int tid) {
+  const int n = (kTK - nvalid) * (512 / 16);
+  for (int idx = tid; idx < n; idx += 256) {
+    const int kr = nvalid + (idx >> 5);
+    *reinterpret_cast<LDS_AS u32x4*>(raw + kr * kRecBytes + 16 * (idx & 31)) = u32x4{0u, 0u, 0u, 0u};
+  }
 }
 
 __device__ __forceinline__ u32x2 lds_read_b64(const LDS_AS uint8_t* p) {
@@ -1414,6 +1409,10 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
       auto iter = [&](auto do_pv_c, auto do_vread_c, int t) {
         constexpr bool DO_PV = decltype(do_pv_c)::value;
         constexpr bool DO_VREAD = decltype(do_vread_c)::value;
+        if (t < ntile) {  // tile t is resident; its V is read in iteration t + 1
+          const int nvalid = min(kTK, t1 - (t0 + t * kTK));
+          if (nvalid < kTK) zero_tail_records_256(smem + kOffRaw + (t & 3) * kRawTileBytes, nvalid, 64 * w + l);
+        }
         const int tp = t - 2;
         uint32_t fl = 0;
         float al[RB];

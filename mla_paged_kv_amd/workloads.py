@@ -40,6 +40,15 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return (r >> np.uint32(16)).astype(np.uint16)
 
 
+def abi_scale(scale=None) -> float:
+    """The softmax scale as the C ABI receives it: a float (fp32) argument.  The
+    workload stores that fp32 value, widened, so the oracle and the kernels see
+    the same number (default 576^-0.5)."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(D_QK)
+    return float(np.float32(scale))
+
+
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
@@ -154,29 +163,34 @@ def dense_workload(name, seed, batch, s_q, h_q, seqlens, pool_pages, std=1.0, ca
         bt[r, :k] = perm[pos:pos + k]
         pos += k
     _seal_pool(pool, bt, seqlens, dtype)
-    if scale is None:
-        scale = 1.0 / math.sqrt(D_QK)
-    return Workload(name=name, seed=seed, batch=batch, s_q=s_q, h_q=h_q, scale=float(scale), causal=causal,
+    return Workload(name=name, seed=seed, batch=batch, s_q=s_q, h_q=h_q, scale=abi_scale(scale), causal=causal,
                     q_bits=q, seqlens=seqlens, kcache_bits=pool, block_table=bt, num_parts=num_parts, dtype=dtype)
 
 
-def _records(rng, n_tokens, chunk=4096):
-    """n_tokens 656-byte records: per 128-dim NoPE block scale = amax/448 (fp32),
-    code = E4M3 of x/scale; RoPE = bf16(x[512:576]); x ~ N(0, 1)."""
+def encode_records(x: np.ndarray) -> np.ndarray:
+    """float32 [n, 576] -> n 656-byte records: per 128-dim NoPE block scale =
+    amax/448 (fp32), code = E4M3 of x/scale; RoPE = bf16(x[512:576])."""
     import torch  # encoding only (float8_e4m3fn cast)
 
+    n = x.shape[0]
+    recs = np.empty((n, REC_BYTES), np.uint8)
+    nope = x[:, :512].reshape(n, 4, 128)
+    amax = np.max(np.abs(nope), axis=2).astype(np.float32)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    y = np.clip(nope / scale[:, :, None], -E4M3_MAX, E4M3_MAX).reshape(n, 512)
+    codes = torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    recs[:, :512] = codes
+    recs[:, 512:528] = scale.astype("<f4").view(np.uint8).reshape(n, 16)
+    recs[:, 528:656] = f32_to_bf16_bits(x[:, 512:]).astype("<u2").view(np.uint8).reshape(n, 128)
+    return recs
+
+
+def _records(rng, n_tokens, chunk=4096):
+    """n_tokens records (encode_records) of x ~ N(0, 1)."""
     recs = np.empty((n_tokens, REC_BYTES), np.uint8)
     for t0 in range(0, n_tokens, chunk):
         t1 = min(n_tokens, t0 + chunk)
-        x = rng.standard_normal(size=(t1 - t0, D_QK), dtype=np.float32)
-        nope = x[:, :512].reshape(t1 - t0, 4, 128)
-        amax = np.max(np.abs(nope), axis=2).astype(np.float32)
-        scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
-        y = np.clip(nope / scale[:, :, None], -E4M3_MAX, E4M3_MAX).reshape(t1 - t0, 512)
-        codes = torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-        recs[t0:t1, :512] = codes
-        recs[t0:t1, 512:528] = scale.astype("<f4").view(np.uint8).reshape(t1 - t0, 16)
-        recs[t0:t1, 528:656] = f32_to_bf16_bits(x[:, 512:]).astype("<u2").view(np.uint8).reshape(t1 - t0, 128)
+        recs[t0:t1] = encode_records(rng.standard_normal(size=(t1 - t0, D_QK), dtype=np.float32))
     return recs
 
 
@@ -202,11 +216,64 @@ def sparse_workload(name, seed, batch, h_q, cap, topk_lengths, context, s_q=1, s
             phys = table[logical // PAGE] * PAGE + logical % PAGE
             n = int(topk[r])
             indices[r, i, :n] = phys[:n].astype(np.int32)
-    if scale is None:
-        scale = 1.0 / math.sqrt(D_QK)
-    return Workload(name=name, seed=seed, batch=batch, s_q=s_q, h_q=h_q, scale=float(scale), causal=False,
+    return Workload(name=name, seed=seed, batch=batch, s_q=s_q, h_q=h_q, scale=abi_scale(scale), causal=False,
                     q_bits=q, seqlens=topk, fp8=True, kcache_rec=recs, indices=indices, topk_capacity=cap,
                     num_parts=num_parts)
+
+
+# --------------------------------------------------------------------------- planted score jumps
+#
+# Inputs whose running score maximum jumps at chosen key positions, so that an
+# online softmax has to move its reference maximum (and rescale what it has
+# accumulated) in the middle of a piece, at a split boundary and in a partial
+# last tile.  Every query row of request r gets a component u_r shared by all
+# its heads and tokens (u_r ~ N(0, 1)^576); a planted key gets beta * u_r / 24
+# added.  With the default scale 1/24 the planted key's score is then about
+# beta + N(0, 2) for every head, against N(0, 2) for the other keys.
+
+
+def _shared_directions(seed, batch):
+    return np.random.default_rng(seed + 7919).standard_normal(size=(batch, D_QK), dtype=np.float32)
+
+
+def plant_dense(w: Workload, plants) -> Workload:
+    """Add the shared component to every query of w and beta * u_r / 24 to key j of
+    request r for each (r, j, beta) in `plants` (positions below seqlen)."""
+    u = _shared_directions(w.seed, w.batch)
+    wide = (lambda b: b.view(np.float16).astype(np.float32)) if w.dtype == "fp16" else bf16_bits_to_f32
+    q = wide(w.q_bits) + u[:, None, None, :]
+    w.q_bits = _to_bits(q, w.dtype)
+    for r, j, beta in plants:
+        assert 0 <= j < int(w.seqlens[r])
+        pg, sl = int(w.block_table[r, j // PAGE]), j % PAGE
+        k = wide(w.kcache_bits[pg, sl]) + np.float32(beta / 24.0) * u[r][None, :]
+        w.kcache_bits[pg, sl] = _to_bits(k, w.dtype)
+    return w
+
+
+def plant_sparse(w: Workload, plants) -> Workload:
+    """The same for a top-k FP8 workload: (r, k, beta) boosts the record selected
+    at top-k position k (k < topk_length[r]) of every query token of request r;
+    the record is re-encoded from its decoded value plus the boost."""
+    u = _shared_directions(w.seed, w.batch)
+    q = bf16_bits_to_f32(w.q_bits) + u[:, None, None, :]
+    w.q_bits = f32_to_bf16_bits(q)
+    flat = w.kcache_rec.reshape(-1, REC_BYTES)
+    import torch  # decoding the E4M3 bytes of the record being re-encoded
+
+    for r, k, beta in plants:
+        assert 0 <= k < int(w.seqlens[r])
+        for i in range(w.s_q):
+            idx = int(w.indices[r, i, k])
+            rec = flat[idx]
+            codes = torch.from_numpy(rec[:512].copy()).view(torch.float8_e4m3fn).float().numpy()
+            sc = rec[512:528].view("<f4").astype(np.float32)
+            x = np.empty(D_QK, np.float32)
+            x[:512] = (codes.reshape(4, 128) * sc[:, None]).reshape(512)
+            x[512:] = bf16_bits_to_f32(rec[528:656].view("<u2"))
+            x += np.float32(beta / 24.0) * u[r]
+            flat[idx] = encode_records(x[None, :])[0]
+    return w
 
 
 # --------------------------------------------------------------------------- named configurations

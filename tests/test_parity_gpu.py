@@ -13,6 +13,7 @@ import torch
 from mla_paged_kv_amd import workloads as W
 from oracle import oracle as O
 from tests import gpu_helpers as G
+from tests import rescale_rule as RR
 
 pytestmark = pytest.mark.gpu
 
@@ -197,19 +198,127 @@ def test_nan_in_unreadable_slots_does_not_leak():
     G.compare("nan-sentinel", out, lse, *ref)
 
 
-# ----------------------------------------------------------------------------- full-size configurations (sampled rows)
+# ----------------------------------------------------------------------------- full-size configurations (every row)
 
-@pytest.mark.parametrize("cfg,sample", [("c3", [0, 17, 63]), ("h", [0, 31, 63]), ("c4", [0, 15])])
-def test_full_size_sampled(cfg, sample):
-    G.say(f"full-size {cfg} sample {sample}")
+@pytest.mark.parametrize("cfg", ["c3", "h", "c4"])
+def test_full_size_every_row(cfg):
+    """The full configurations at the library's split count, every output row
+    against the oracle."""
+    G.say(f"full-size {cfg}")
     w = W.config(cfg)
     out, lse, plan = G.run_dense(w)
     G.say(f"  num_parts={plan.num_parts}")
-    o, l = G.to_np(out, lse)
-    s = G.sub_workload(w, sample)
-    ref = oracle_dense(s)
-    G.compare(f"{cfg}-sampled", o[sample], l[sample], *ref)
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+    G.compare(f"{cfg}-full", out, lse, *oracle_dense(w))
+    assert ops.mla_read_device_errors() == 0
+
+
+# ----------------------------------------------------------------------------- long pieces, many splits
+
+@pytest.mark.parametrize("parts", [1, None], ids=["one-piece", "library-parts"])
+def test_long_context_sk65536(parts):
+    """b=1, sk=65536 (1024 pages; the dense page's longest sweep point).  With one
+    piece the request spans more pages than a workgroup caches, so the later page
+    ids come from the direct lookup path."""
+    G.say(f"sk=65536 parts={parts}")
+    w = W.dense_workload("sk65536", 196, 1, 1, 128, [65536], pool_pages=1100, num_parts=parts)
+    out, lse, plan = G.run_dense(w)
+    G.say(f"  num_parts={plan.num_parts}")
+    G.compare(f"sk65536-p{plan.num_parts}", out, lse, *oracle_dense(w))
+    assert ops.mla_read_device_errors() == 0
+
+
+@pytest.mark.parametrize("parts", [128, 200])
+def test_combine_more_than_64_splits(parts):
+    """One request cut into more than 64 splits: the combine's lse reductions
+    run over several groups of 64."""
+    G.say(f"sk=16384 cut into {parts} splits")
+    w = W.dense_workload("many-splits", 197, 1, 1, 128, [16384], pool_pages=300, num_parts=parts)
+    out, lse, plan = G.run_dense(w)
+    splits = int(plan.num_splits.cpu().numpy()[1])
+    assert splits == parts > 64
+    G.compare(f"splits{parts}", out, lse, *oracle_dense(w))
+
+
+# ----------------------------------------------------------------------------- online-softmax rescale branch
+#
+# With N(0, 1) inputs a row's score maximum never climbs 8 log2 units after a
+# piece's first tile, so the rescale branch of the online softmax would never
+# run.  These workloads plant high-scoring keys (tests/rescale_rule.py counts
+# the resulting moves of the reference maximum with the kernels' own rule, and
+# each test asserts there are some) in the middle of pieces, at the first key of
+# a split, and in a partial last tile.
+
+RESCALE_DENSE = [
+    # name, seed, b, s_q, h_q, seqlens, pool pages, causal, forced parts, plants (request, key, beta), dtype, h_kv
+    ("bf16-h128-p5", 190, 3, 1, 128, [1, 700, 2049], 60, False, 5,
+     [(1, 150, 15.0), (1, 512, 30.0), (1, 699, 45.0), (2, 300, 12.0), (2, 960, 27.0), (2, 1100, 40.0),
+      (2, 2048, 55.0)], "bf16", 1),
+    ("bf16-h128-library", 191, 2, 1, 128, [4096, 1500], 100, False, None,
+     [(0, 40, 12.0), (0, 1000, 26.0), (0, 2100, 40.0), (0, 4095, 55.0), (1, 700, 20.0), (1, 1499, 35.0)],
+     "bf16", 1),
+    ("bf16-h64-causal-sq2", 192, 2, 2, 64, [300, 1000], 30, True, 3,
+     [(0, 100, 14.0), (0, 298, 30.0), (0, 299, 44.0), (1, 500, 13.0), (1, 998, 28.0), (1, 999, 43.0)], "bf16", 1),
+    ("bf16-h16-p1", 193, 2, 1, 16, [333, 200], 10, False, 1,
+     [(0, 70, 15.0), (0, 332, 30.0), (1, 130, 20.0), (1, 199, 36.0)], "bf16", 1),
+    ("bf16-hkv2-h128", 194, 2, 1, 128, [900, 400], 24, False, 3,
+     [(0, 300, 15.0), (0, 899, 32.0), (1, 399, 20.0)], "bf16", 2),
+    ("fp16-h128-p4", 195, 2, 1, 128, [1000, 333], 24, False, 4,
+     [(0, 200, 14.0), (0, 640, 28.0), (0, 999, 42.0), (1, 100, 15.0), (1, 332, 30.0)], "fp16", 1),
+]
+
+
+@pytest.mark.parametrize("case", RESCALE_DENSE, ids=[c[0] for c in RESCALE_DENSE])
+def test_rescale_branch_dense(case):
+    name, seed, b, s_q, h_q, seqlens, pool, causal, parts, plants, dtype, h_kv = case
+    G.say(f"rescale dense {name}")
+    w = W.dense_workload(name, seed, b, s_q, h_q, seqlens, pool_pages=pool, causal=causal, dtype=dtype, h_kv=h_kv)
+    W.plant_dense(w, plants)
+    fmt = ops.KV_FP16_PAGED if dtype == "fp16" else ops.KV_BF16_PAGED
+    P = parts or ops.mla_decode_num_parts(b, s_q, h_q, h_kv, fmt)
+    moves, ambiguous = RR.moves_for(w, P)
+    G.say(f"  num_parts={P}: {moves} moves of the reference max after a piece's first tile "
+          f"({ambiguous} comparisons within 0.5 of the threshold)")
+    assert moves > 0
+    t = G.dev_tensors(w)
+    plan = ops.DecodePlan(t["seqlens"], s_q, h_q, fmt, num_parts=P, h_kv=h_kv)
+    out, lse = ops.mla_decode(t["q"], t["kcache"], t["block_table"], t["seqlens"], w.scale, w.causal, plan=plan,
+                              kv_format=fmt)
+    torch.cuda.synchronize()
+    G.compare(name, out, lse, *oracle_dense(w))
+
+
+RESCALE_SPARSE = [
+    # name, seed, b, h_q, cap, topk lengths, context, s_q, forced parts, plants (request, top-k position, beta)
+    ("h64-tails", 200, 3, 64, 192, [192, 65, 100], 4096, 1, 4,
+     [(0, 40, 14.0), (0, 64, 28.0), (0, 191, 42.0), (1, 64, 20.0), (2, 70, 15.0), (2, 99, 30.0)]),
+    ("h128-topk2048", 201, 2, 128, 2048, [2048, 1800], 32768, 1, None,
+     [(0, 100, 12.0), (0, 1024, 26.0), (0, 2047, 40.0), (1, 900, 15.0), (1, 1799, 30.0)]),
+    ("h64-sq2", 202, 2, 64, 256, [256, 130], 2048, 2, 3,
+     [(0, 10, 13.0), (0, 255, 30.0), (1, 129, 20.0)]),
+]
+
+
+@pytest.mark.parametrize("case", RESCALE_SPARSE, ids=[c[0] for c in RESCALE_SPARSE])
+def test_rescale_branch_fp8(case):
+    """The FP8 kernel's own online softmax (packed workspace and gathered by
+    index) through the rescale branch, against the oracle and bitwise with each
+    other."""
+    name, seed, b, h, cap, topk, ctx, s_q, parts, plants = case
+    G.say(f"rescale fp8 {name}")
+    w = W.sparse_workload(name, seed, b, h, cap, topk, context=ctx, s_q=s_q, num_parts=parts)
+    W.plant_sparse(w, plants)
+    P = parts or ops.mla_decode_num_parts(b, s_q, h, 1, ops.KV_FP8_PACKED)
+    moves, ambiguous = RR.moves_for(w, P)
+    G.say(f"  num_parts={P}: {moves} moves of the reference max after a piece's first tile "
+          f"({ambiguous} comparisons within 0.5 of the threshold)")
+    assert moves > 0
+    t = G.dev_tensors(w)
+    ref = oracle_sparse(w)
+    out_p, lse_p, _, plan_p = G.run_sparse(w, t, num_parts=P)
+    G.compare(name + "-packed", out_p, lse_p, *ref)
+    out_i, lse_i, plan_i = G.run_sparse_indexed(w, t, num_parts=P)
+    G.compare(name + "-indexed", out_i, lse_i, *ref)
+    assert torch.equal(out_p, out_i) and torch.equal(lse_p, lse_i)
 
 
 # ----------------------------------------------------------------------------- combine alone
@@ -409,6 +518,35 @@ def test_fp8_indexed_config_c5():
     G.compare("c5-indexed", out, lse, *oracle_sparse(w))
     out_p, lse_p, _, _ = G.run_sparse(w, t)
     assert torch.equal(out, out_p) and torch.equal(lse, lse_p)
+
+
+def test_fp8_nan_records_never_reach_the_output():
+    """Records no row selects, including record 0 (which the by-index loader reads
+    for keys past topk_length), hold E4M3 NaN bytes (0x7F / 0xFF): the by-index
+    decode still matches the oracle and, bit for bit, the pack + packed decode."""
+    G.say("fp8: NaN bytes in unselected records")
+    w = W.sparse_workload("nan-pool", 157, 3, 64, 192, [150, 33, 192], context=2048)
+    flat = w.kcache_rec.reshape(-1, 656)
+    chosen = set()
+    for r in range(w.batch):
+        for i in range(w.s_q):
+            chosen.update(int(x) for x in w.indices[r, i, :int(w.seqlens[r])])
+    if 0 in chosen:  # keep record 0 unselected: swap its selection for a free id of the same page range
+        free = next(x for x in range(1, 32 * 64) if x not in chosen)
+        w.indices[w.indices == 0] = free
+        chosen.discard(0)
+        chosen.add(free)
+    unselected = np.array(sorted(set(range(flat.shape[0])) - chosen))
+    flat[unselected, :512] = np.where(np.arange(512) % 2 == 0, 0x7F, 0xFF).astype(np.uint8)
+    assert 0 in set(unselected.tolist())
+    ref = oracle_sparse(w)  # the oracle reads selected records only
+    t = G.dev_tensors(w)
+    out_i, lse_i, _ = G.run_sparse_indexed(w, t)
+    G.compare("nan-pool-indexed", out_i, lse_i, *ref)
+    out_p, lse_p, _, _ = G.run_sparse(w, t)
+    G.compare("nan-pool-packed", out_p, lse_p, *ref)
+    assert torch.equal(out_i, out_p) and torch.equal(lse_i, lse_p)
+    assert ops.mla_read_device_errors() == 0
 
 
 def test_fp8_indexed_ignores_ids_past_topk_length():
