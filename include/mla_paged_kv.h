@@ -242,6 +242,27 @@ int mla_decode_fwd(const void* q, const void* kv, int kv_format, int64_t num_pag
 int mla_combine(const int32_t* num_splits, const void* workspace, size_t workspace_bytes, int batch, int s_q,
                 int h_q, int num_parts, int kv_format, void* out, float* lse, void* stream);
 
+/* Decode + combine with no caller workspace (device), for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, scope, kernels and results
+ * as mla_decode_fwd followed by mla_combine on `stream`, except that the split
+ * partials live in a device array the library owns: 128 MiB
+ * (MLA_NOALLOC_SCRATCH_BYTES) per device, reserved when the library's device
+ * code is loaded on that device and held until the process ends.  The call
+ * itself allocates nothing.  mla_decode_workspace_size(batch, s_q, h_q,
+ * num_parts) must not exceed that size, else MLA_ERR_WORKSPACE_TOO_SMALL
+ * before any launch (use fewer parts or a smaller batch).  Every call on one
+ * device shares that device's array and leaves its last contents there (every
+ * slot a call reads is first written by that call's decode); calls whose
+ * execution overlaps on one device (concurrent streams, or host threads using
+ * one device) race on it and must be serialised by the caller. */
+#define MLA_NOALLOC_SCRATCH_BYTES (((size_t)128) << 20)
+int mla_decode_fwd_noalloc(const void* q, const void* kv, int kv_format, int64_t num_pages,
+                           const int32_t* block_table, int max_pages, const int32_t* seqlens, int topk_capacity,
+                           int batch, int s_q, int h_q, int h_kv, float softmax_scale, int causal,
+                           const int32_t* sched_meta, const int32_t* num_splits, int num_parts, void* out, float* lse,
+                           void* stream);
+
 /* Pack (device): the packing kernel of "[SM90] Add packed selected-KV sparse
  * decode" (FlashMLA PR 200, "SM90 packing kernel": selected 656-byte records
  * copied byte for byte into a 64-token tile-major workspace, invalid suffix

@@ -93,6 +93,92 @@ int check_shape(int batch, int s_q, int h_q, int h_kv, int kv_format) {
 
 int slots_for(int batch, int num_parts) { return batch + num_parts; }
 
+// Argument checks of the decode entry points (everything but the workspace).
+int check_decode_args(const void* q, const void* kv, int kv_format, int64_t num_pages, const int32_t* block_table,
+                      int max_pages, const int32_t* seqlens, int topk_capacity, int batch, int s_q, int h_q, int h_kv,
+                      float softmax_scale, const int32_t* sched_meta, const int32_t* num_splits, int num_parts,
+                      const void* out, const float* lse, int causal) {
+  if (!q || !kv || !seqlens || !sched_meta || !num_splits || !out || !lse)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  int st = check_shape(batch, s_q, h_q, h_kv, kv_format);
+  if (st) return st;
+  const bool fp8 = kv_format == MLA_KV_FP8_PACKED || kv_format == MLA_KV_FP8_INDEXED;
+  if (fp8) {
+    if (topk_capacity < mla::kPage || topk_capacity % mla::kPage != 0)
+      return fail(MLA_ERR_UNSUPPORTED, "topk_capacity %d must be a positive multiple of 64", topk_capacity);
+    if (causal) return fail(MLA_ERR_UNSUPPORTED, "sparse FP8 decode has no causal mask");
+    if (kv_format == MLA_KV_FP8_INDEXED) {
+      if (!block_table) return fail(MLA_ERR_INVALID_ARGUMENT, "indices (block_table argument) is NULL");
+      if (num_pages < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "num_pages %lld < 1", (long long)num_pages);
+      if (num_pages > INT64_MAX / (mla::kPage * mla::kRecBytes)) return fail(MLA_ERR_UNSUPPORTED, "num_pages too large");
+    }
+  } else {
+    if (!block_table) return fail(MLA_ERR_INVALID_ARGUMENT, "block_table is NULL");
+    if (max_pages < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "max_pages %d < 1", max_pages);
+    if (num_pages < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "num_pages %lld < 1", (long long)num_pages);
+    if ((int64_t)batch * max_pages > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "batch * max_pages above 2^31");
+    if ((int64_t)max_pages * mla::kPage > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "max_pages too large");
+  }
+  if (num_parts < 1 || num_parts > MLA_MAX_PARTS)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "num_parts %d out of [1, %d]", num_parts, MLA_MAX_PARTS);
+  if (!(softmax_scale > 0.f) || !(softmax_scale < INFINITY))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0 (got %g)", (double)softmax_scale);
+  return MLA_OK;
+}
+
+// Decode launch on validated arguments; `workspace` holds the split partials
+// (at least mla_decode_workspace_size bytes).
+int launch_decode_checked(const void* q, const void* kv, int kv_format, int64_t num_pages, const int32_t* block_table,
+                          int max_pages, const int32_t* seqlens, int topk_capacity, int batch, int s_q, int h_q,
+                          int h_kv, float softmax_scale, int causal, const int32_t* sched_meta,
+                          const int32_t* num_splits, int num_parts, void* out, float* lse, void* workspace,
+                          hipStream_t stream) {
+  mla::DecodeArgs a;
+  a.q = (const uint16_t*)q;
+  a.kv = (const uint8_t*)kv;
+  a.num_pages = num_pages;
+  a.block_table = block_table;
+  a.max_pages = max_pages;
+  a.seqlens = seqlens;
+  a.cap = topk_capacity;
+  a.batch = batch;
+  a.s_q = s_q;
+  a.h_q = h_q;
+  a.M = s_q * h_q;
+  a.h_kv = h_kv;
+  a.G = h_q / h_kv;
+  a.Mkv = s_q * a.G;
+  a.scale_log2 = softmax_scale * 1.44269504088896340736f;
+  a.causal = causal ? 1 : 0;
+  a.sched_meta = sched_meta;
+  a.num_splits = num_splits;
+  a.num_parts = num_parts;
+  a.out = (uint16_t*)out;
+  a.lse = lse;
+  a.slots = slots_for(batch, num_parts);
+  a.part_o = (float*)workspace;
+  a.part_lse = a.part_o + (size_t)a.slots * a.M * mla::kDV;
+  const int kind = kv_format == MLA_KV_FP8_PACKED    ? mla::kDecodeFp8Packed
+                   : kv_format == MLA_KV_FP8_INDEXED ? mla::kDecodeFp8Indexed
+                   : kv_format == MLA_KV_FP16_PAGED  ? mla::kDecodeF16
+                                                     : mla::kDecodeBf16;
+  hipError_t e = mla::launch_decode(a, kind, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
+}
+
+// Combine launch on validated arguments.
+int launch_combine_checked(const int32_t* num_splits, const void* workspace, int batch, int s_q, int h_q,
+                           int num_parts, int kv_format, void* out, float* lse, hipStream_t stream) {
+  const int M = s_q * h_q;
+  const float* part_o = (const float*)workspace;
+  const float* part_lse = part_o + (size_t)slots_for(batch, num_parts) * M * mla::kDV;
+  hipError_t e = mla::launch_combine(num_splits, part_o, part_lse, batch, M, slots_for(batch, num_parts),
+                                     kv_format == MLA_KV_FP16_PAGED, (uint16_t*)out, lse, stream);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -190,69 +276,17 @@ int mla_decode_fwd(const void* q, const void* kv, int kv_format, int64_t num_pag
                    int max_pages, const int32_t* seqlens, int topk_capacity, int batch, int s_q, int h_q, int h_kv,
                    float softmax_scale, int causal, const int32_t* sched_meta, const int32_t* num_splits,
                    int num_parts, void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !kv || !seqlens || !sched_meta || !num_splits || !out || !lse)
-    return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
-  int st = check_shape(batch, s_q, h_q, h_kv, kv_format);
+  int st = check_decode_args(q, kv, kv_format, num_pages, block_table, max_pages, seqlens, topk_capacity, batch, s_q,
+                             h_q, h_kv, softmax_scale, sched_meta, num_splits, num_parts, out, lse, causal);
   if (st) return st;
-  const bool fp8 = kv_format == MLA_KV_FP8_PACKED || kv_format == MLA_KV_FP8_INDEXED;
-  if (fp8) {
-    if (topk_capacity < mla::kPage || topk_capacity % mla::kPage != 0)
-      return fail(MLA_ERR_UNSUPPORTED, "topk_capacity %d must be a positive multiple of 64", topk_capacity);
-    if (causal) return fail(MLA_ERR_UNSUPPORTED, "sparse FP8 decode has no causal mask");
-    if (kv_format == MLA_KV_FP8_INDEXED) {
-      if (!block_table) return fail(MLA_ERR_INVALID_ARGUMENT, "indices (block_table argument) is NULL");
-      if (num_pages < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "num_pages %lld < 1", (long long)num_pages);
-      if (num_pages > INT64_MAX / (mla::kPage * mla::kRecBytes)) return fail(MLA_ERR_UNSUPPORTED, "num_pages too large");
-    }
-  } else {
-    if (!block_table) return fail(MLA_ERR_INVALID_ARGUMENT, "block_table is NULL");
-    if (max_pages < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "max_pages %d < 1", max_pages);
-    if (num_pages < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "num_pages %lld < 1", (long long)num_pages);
-    if ((int64_t)batch * max_pages > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "batch * max_pages above 2^31");
-    if ((int64_t)max_pages * mla::kPage > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "max_pages too large");
-  }
-  if (num_parts < 1 || num_parts > MLA_MAX_PARTS)
-    return fail(MLA_ERR_INVALID_ARGUMENT, "num_parts %d out of [1, %d]", num_parts, MLA_MAX_PARTS);
-  if (!(softmax_scale > 0.f) || !(softmax_scale < INFINITY))
-    return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0 (got %g)", (double)softmax_scale);
   const size_t need = mla_decode_workspace_size(batch, s_q, h_q, num_parts);
   if (!workspace || workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "decode workspace %zu B < %zu B", workspace_bytes, need);
   st = check_device();
   if (st) return st;
-
-  mla::DecodeArgs a;
-  a.q = (const uint16_t*)q;
-  a.kv = (const uint8_t*)kv;
-  a.num_pages = num_pages;
-  a.block_table = block_table;
-  a.max_pages = max_pages;
-  a.seqlens = seqlens;
-  a.cap = topk_capacity;
-  a.batch = batch;
-  a.s_q = s_q;
-  a.h_q = h_q;
-  a.M = s_q * h_q;
-  a.h_kv = h_kv;
-  a.G = h_q / h_kv;
-  a.Mkv = s_q * a.G;
-  a.scale_log2 = softmax_scale * 1.44269504088896340736f;
-  a.causal = causal ? 1 : 0;
-  a.sched_meta = sched_meta;
-  a.num_splits = num_splits;
-  a.num_parts = num_parts;
-  a.out = (uint16_t*)out;
-  a.lse = lse;
-  a.slots = slots_for(batch, num_parts);
-  a.part_o = (float*)workspace;
-  a.part_lse = a.part_o + (size_t)a.slots * a.M * mla::kDV;
-  const int kind = kv_format == MLA_KV_FP8_PACKED    ? mla::kDecodeFp8Packed
-                   : kv_format == MLA_KV_FP8_INDEXED ? mla::kDecodeFp8Indexed
-                   : kv_format == MLA_KV_FP16_PAGED  ? mla::kDecodeF16
-                                                     : mla::kDecodeBf16;
-  hipError_t e = mla::launch_decode(a, kind, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "decode launch");
-  return ok();
+  return launch_decode_checked(q, kv, kv_format, num_pages, block_table, max_pages, seqlens, topk_capacity, batch,
+                               s_q, h_q, h_kv, softmax_scale, causal, sched_meta, num_splits, num_parts, out, lse,
+                               workspace, (hipStream_t)stream);
 }
 
 int mla_combine(const int32_t* num_splits, const void* workspace, size_t workspace_bytes, int batch, int s_q,
@@ -266,13 +300,34 @@ int mla_combine(const int32_t* num_splits, const void* workspace, size_t workspa
   if (workspace_bytes < need) return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "decode workspace %zu B < %zu B", workspace_bytes, need);
   st = check_device();
   if (st) return st;
-  const int M = s_q * h_q;
-  const float* part_o = (const float*)workspace;
-  const float* part_lse = part_o + (size_t)slots_for(batch, num_parts) * M * mla::kDV;
-  hipError_t e = mla::launch_combine(num_splits, part_o, part_lse, batch, M, slots_for(batch, num_parts),
-                                     kv_format == MLA_KV_FP16_PAGED, (uint16_t*)out, lse, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "combine launch");
-  return ok();
+  return launch_combine_checked(num_splits, workspace, batch, s_q, h_q, num_parts, kv_format, out, lse,
+                                (hipStream_t)stream);
+}
+
+int mla_decode_fwd_noalloc(const void* q, const void* kv, int kv_format, int64_t num_pages,
+                           const int32_t* block_table, int max_pages, const int32_t* seqlens, int topk_capacity,
+                           int batch, int s_q, int h_q, int h_kv, float softmax_scale, int causal,
+                           const int32_t* sched_meta, const int32_t* num_splits, int num_parts, void* out, float* lse,
+                           void* stream) {
+  int st = check_decode_args(q, kv, kv_format, num_pages, block_table, max_pages, seqlens, topk_capacity, batch, s_q,
+                             h_q, h_kv, softmax_scale, sched_meta, num_splits, num_parts, out, lse, causal);
+  if (st) return st;
+  const size_t need = mla_decode_workspace_size(batch, s_q, h_q, num_parts);
+  if (need > mla::kNoAllocScratchBytes)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL,
+                "split partials need %zu B, above the %zu B of library scratch (fewer parts, or a smaller batch)",
+                need, mla::kNoAllocScratchBytes);
+  st = check_device();
+  if (st) return st;
+  void* ws = nullptr;
+  hipError_t e = mla::noalloc_scratch(&ws);
+  if (e != hipSuccess) return hip_fail(e, "library scratch lookup");
+  st = launch_decode_checked(q, kv, kv_format, num_pages, block_table, max_pages, seqlens, topk_capacity, batch, s_q,
+                             h_q, h_kv, softmax_scale, causal, sched_meta, num_splits, num_parts, out, lse, ws,
+                             (hipStream_t)stream);
+  if (st) return st;
+  return launch_combine_checked(num_splits, ws, batch, s_q, h_q, num_parts, kv_format, out, lse,
+                                (hipStream_t)stream);
 }
 
 int mla_pack_selected_kv(const void* kcache_fp8, int64_t num_pages, const int32_t* indices,

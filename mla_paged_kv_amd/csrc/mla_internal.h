@@ -63,4 +63,10 @@ constexpr int kPatchMaxNewIds = 64;
 hipError_t decode_occupancy(int kind, int M, int* wgs_per_cu);
 hipError_t read_and_clear_error_flags(int* flags, hipStream_t stream);
 
+// Device scratch of the entry point that allocates nothing (split partials):
+// a file-scope __device__ array of this many bytes per device.  *ptr receives
+// the current device's address of it (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace mla

@@ -29,6 +29,7 @@
 //     key's fp32 block scales multiply the per-block score sums and P.
 #include "mla_internal.h"
 
+#include <mutex>
 #include <type_traits>
 
 #include <math.h>
@@ -1760,6 +1761,35 @@ hipError_t launch_patch(const uint8_t* kcache, int64_t num_pages, const int32_t*
   hipLaunchKernelGGL(patch_kernel, grid, dim3(64), 0, stream, kcache, num_pages, indices, topk_length, new_ids, n_new,
                      s_q, cap, ws);
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ scratch for the entry point that allocates nothing
+// Split partials of mla_decode_fwd_noalloc live here instead of in a caller
+// workspace.  Each device holds its own copy of the array (at its own address)
+// from the module load until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current and
+// kept below; only that address is ever passed to a kernel.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t read_and_clear_error_flags(int* flags, hipStream_t stream) {

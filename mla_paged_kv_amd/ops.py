@@ -37,6 +37,7 @@ KV_FP8_INDEXED = 2
 KV_FP16_PAGED = 3
 SCHED_AUTO, SCHED_GLOBAL, SCHED_REQUEST_LOCAL = 0, 1, 2
 D_QK, D_V, PAGE, REC_BYTES = 576, 512, 64, 656
+NOALLOC_SCRATCH_BYTES = 128 << 20  # MLA_NOALLOC_SCRATCH_BYTES
 SCHED_META_INTS = 8
 
 _P = ctypes.c_void_p
@@ -52,6 +53,8 @@ _SIGS = {
     "mla_decode_fwd": ([_P, _P, _i32, _i64, _P, _i32, _P, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _P, _P, _i32,
                         _P, _P, _P, _sz, _P], _i32),
     "mla_combine": ([_P, _P, _sz, _i32, _i32, _i32, _i32, _i32, _P, _P, _P], _i32),
+    "mla_decode_fwd_noalloc": ([_P, _P, _i32, _i64, _P, _i32, _P, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _P, _P,
+                                _i32, _P, _P, _P], _i32),
     "mla_pack_selected_kv": ([_P, _i64, _P, _P, _i32, _i32, _i32, _P, _sz, _P], _i32),
     "mla_patch_packed_kv": ([_P, _i64, _P, _P, _i32, _i32, _i32, _P, _i32, _P, _sz, _P], _i32),
     "mla_sparse_kv_format": ([_i32, _i32, _i32, _sz, _i32, _P], _i32),
@@ -160,8 +163,8 @@ def mla_get_packed_decode_metadata(topk_length, batch, s_q, h_q, topk_capacity, 
     return sched_meta, num_splits
 
 
-def mla_decode_fwd(q, kv, kv_format, block_table, seqlens, softmax_scale, causal, sched_meta, num_splits, out, lse,
-                   workspace, topk_capacity=0, stream=None):
+def _decode_args(q, kv, kv_format, block_table, seqlens, sched_meta, num_splits, out, lse, topk_capacity):
+    """Checks of the decode entry points' tensors; returns the sizes they pass."""
     _need(q, "q", _act_dtype(kv_format))
     b, s_q, h_q, d = q.shape
     if d != D_QK:
@@ -197,12 +200,31 @@ def mla_decode_fwd(q, kv, kv_format, block_table, seqlens, softmax_scale, causal
     _need(num_splits, "num_splits", torch.int32, (b + 1,))
     _need(out, "out", _act_dtype(kv_format), (b, s_q, h_q, D_V))
     _need(lse, "lse", torch.float32, (b, s_q, h_q))
+    return b, s_q, h_q, h_kv, num_pages, max_pages, topk_capacity
+
+
+def mla_decode_fwd(q, kv, kv_format, block_table, seqlens, softmax_scale, causal, sched_meta, num_splits, out, lse,
+                   workspace, topk_capacity=0, stream=None):
+    args = _decode_args(q, kv, kv_format, block_table, seqlens, sched_meta, num_splits, out, lse, topk_capacity)
+    b, s_q, h_q, h_kv, num_pages, max_pages, topk_capacity = args
     _need(workspace, "workspace", torch.uint8)
     _check(_lib.mla_decode_fwd(
         _ptr(q), _ptr(kv), kv_format, num_pages, _ptr(block_table) if kv_format != KV_FP8_PACKED else None,
         max_pages, _ptr(seqlens), topk_capacity, b, s_q, h_q, h_kv, float(softmax_scale), int(bool(causal)),
         _ptr(sched_meta), _ptr(num_splits), sched_meta.shape[0], _ptr(out), _ptr(lse), _ptr(workspace),
         workspace.numel(), _stream(stream)))
+
+
+def mla_decode_fwd_noalloc(q, kv, kv_format, block_table, seqlens, softmax_scale, causal, sched_meta, num_splits,
+                           out, lse, topk_capacity=0, stream=None):
+    """mla_decode_fwd + mla_combine with the split partials in the library's own
+    device scratch (no workspace argument, nothing allocated by the call)."""
+    args = _decode_args(q, kv, kv_format, block_table, seqlens, sched_meta, num_splits, out, lse, topk_capacity)
+    b, s_q, h_q, h_kv, num_pages, max_pages, topk_capacity = args
+    _check(_lib.mla_decode_fwd_noalloc(
+        _ptr(q), _ptr(kv), kv_format, num_pages, _ptr(block_table) if kv_format != KV_FP8_PACKED else None,
+        max_pages, _ptr(seqlens), topk_capacity, b, s_q, h_q, h_kv, float(softmax_scale), int(bool(causal)),
+        _ptr(sched_meta), _ptr(num_splits), sched_meta.shape[0], _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def mla_combine(num_splits, workspace, batch, s_q, h_q, num_parts, out, lse, stream=None, kv_format=KV_BF16_PAGED):
