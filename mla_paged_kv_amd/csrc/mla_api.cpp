@@ -192,7 +192,11 @@ int mla_plan_num_parts(int batch, int s_q, int h_q, int h_kv, int kv_format, int
   if (st) return st;
   if (cus < 1 || wgs_per_cu < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "cus %d / wgs_per_cu %d must be >= 1", cus, wgs_per_cu);
   const int Mkv = s_q * (h_q / h_kv);  // rows per (request, KV head)
-  const int rb = 16 * mla::decode_row_blocks_per_wg(Mkv);
+  const int kind = kv_format == MLA_KV_FP8_PACKED    ? mla::kDecodeFp8Packed
+                   : kv_format == MLA_KV_FP8_INDEXED ? mla::kDecodeFp8Indexed
+                   : kv_format == MLA_KV_FP16_PAGED  ? mla::kDecodeF16
+                                                     : mla::kDecodeBf16;
+  const int rb = mla::decode_rows_per_wg(s_q * h_q, h_kv, kind);
   const int row_blocks = h_kv * ((Mkv + rb - 1) / rb);
   int64_t slots = (int64_t)cus * wgs_per_cu;
   int64_t parts = slots / row_blocks;

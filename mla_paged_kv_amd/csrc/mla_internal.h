@@ -43,8 +43,18 @@ struct DecodeArgs {
   int slots;
 };
 
-// Rows per workgroup for M rows per request: 16 * RB with RB in {1,2,4,8}.
+// Rows per workgroup of the 64-row kernel family for M rows per request:
+// 16 * RB with RB in {1, 2, 4}.
 int decode_row_blocks_per_wg(int M);
+
+// The 128-row dense kernel (mla_decode_r128.hip): bf16 / fp16 pages, one KV
+// head, M a multiple of 128.  One workgroup per (part, 128-row block).
+bool decode_r128_shape(int M, int h_kv, int kind);
+hipError_t launch_decode_r128(const struct DecodeArgs& a, int kind, hipStream_t stream);
+hipError_t decode_r128_occupancy(int kind, int* wgs_per_cu);
+hipError_t read_and_clear_error_flags_r128(int* flags);
+// Query rows one decode workgroup covers for this shape (either kernel family).
+int decode_rows_per_wg(int M, int h_kv, int kind);
 
 hipError_t launch_sched(const int32_t* lengths, int batch, int num_parts, int32_t* meta, int32_t* num_splits,
                         hipStream_t stream, bool request_local = false);

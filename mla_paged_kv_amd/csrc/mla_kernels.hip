@@ -1519,7 +1519,13 @@ static hipError_t launch_decode_t(const DecodeArgs& a, int kind, hipStream_t str
   return hipGetLastError();
 }
 
+int decode_rows_per_wg(int M, int h_kv, int kind) {
+  if (decode_r128_shape(M, h_kv, kind)) return 128;
+  return 16 * decode_row_blocks_per_wg(h_kv > 1 ? M / h_kv : M);
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int kind, hipStream_t stream) {
+  if (decode_r128_shape(a.M, a.h_kv, kind)) return launch_decode_r128(a, kind, stream);
   switch (decode_row_blocks_per_wg(a.h_kv > 1 ? a.Mkv : a.M)) {
     case 1: return launch_decode_t<1>(a, kind, stream);
     case 2: return launch_decode_t<2>(a, kind, stream);
@@ -1542,6 +1548,11 @@ static hipError_t occupancy_t(int kind, int* n) {
 hipError_t decode_occupancy(int kind, int M, int* wgs_per_cu) {
   int n = 0;
   hipError_t e;
+  if (decode_r128_shape(M, 1, kind)) {
+    e = decode_r128_occupancy(kind, &n);
+    *wgs_per_cu = n;
+    return e;
+  }
   switch (decode_row_blocks_per_wg(M)) {
     case 1: e = occupancy_t<1>(kind, &n); break;
     case 2: e = occupancy_t<2>(kind, &n); break;
@@ -1800,7 +1811,10 @@ hipError_t read_and_clear_error_flags(int* flags, hipStream_t stream) {
   if (e != hipSuccess) return e;
   int zero = 0;
   e = hipMemcpyToSymbol(HIP_SYMBOL(g_error_flags), &zero, sizeof(int), 0, hipMemcpyHostToDevice);
-  *flags = v;
+  if (e != hipSuccess) return e;
+  int v2 = 0;
+  e = read_and_clear_error_flags_r128(&v2);
+  *flags = v | v2;
   return e;
 }
 

@@ -53,10 +53,12 @@ def test_decode_workspace_size_formula():
 
 
 @pytest.mark.parametrize("batch,s_q,h_q,cus,wgs,expect", [
-    (64, 1, 128, 256, 1, 128),      # two 64-row blocks per request -> 256 WG slots / 2
+    (64, 1, 128, 256, 1, 128),      # 64-row kernel: two row blocks per request -> 256 WG slots / 2
     (1, 1, 128, 256, 1, 16),        # capped at 16 pieces per request
-    (8, 1, 64, 256, 1, 128),        # 8 requests x 16
-    (16, 2, 128, 256, 1, 64),       # 4 row blocks per request
+    (8, 1, 64, 256, 1, 128),        # 64-row kernel, one row block: 8 requests x 16
+    (16, 2, 128, 256, 1, 128),      # 256 rows: 128-row kernel, two row blocks per request
+    (4, 4, 128, 256, 1, 64),        # 512 rows: four 128-row blocks, 4 x 16
+    (4, 1, 96, 256, 1, 64),         # 96 rows: two 64-row blocks (64-row kernel), 4 x 16
     (1, 1, 16, 256, 1, 16),
     (1000, 1, 128, 256, 1, 128),
 ])

@@ -137,7 +137,12 @@ def test_dense_multi_kv_head(case):
         plan1 = ops.DecodePlan(t["seqlens"], s_q, g, fmt, num_parts=P)
         o1, l1 = ops.mla_decode(qg, kg, t["block_table"], t["seqlens"], w.scale, w.causal, plan=plan1, kv_format=fmt)
         torch.cuda.synchronize()
-        assert torch.equal(o1, out[:, :, kk * g:(kk + 1) * g]) and torch.equal(l1, lse[:, :, kk * g:(kk + 1) * g])
+        og, lg = out[:, :, kk * g:(kk + 1) * g], lse[:, :, kk * g:(kk + 1) * g]
+        if not G.uses_r128_kernel(s_q * g):  # 64-row kernel family on both sides: same arithmetic
+            assert torch.equal(o1, og) and torch.equal(l1, lg)
+        else:  # the group alone runs on the 128-row kernel: another summation order
+            assert torch.allclose(o1.float(), og.float(), atol=1e-2, rtol=1e-2)
+            assert torch.allclose(l1, lg, atol=1e-3, rtol=0)
 
 
 @pytest.mark.parametrize("cfg", ["c1", "c2"])
