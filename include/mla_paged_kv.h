@@ -116,6 +116,13 @@ int mla_decode_num_parts(int batch, int s_q, int h_q, int h_kv, int kv_format, i
 int mla_plan_num_parts(int batch, int s_q, int h_q, int h_kv, int kv_format, int cus, int wgs_per_cu,
                        int* num_parts_out);
 
+/* Name of the decode kernel instantiation mla_decode_fwd launches for this
+ * shape and format, as profilers print it without namespaces and parameters
+ * (e.g. "decode_ws_kernel<4, false, false>"), so that a profile or a timing can
+ * be attributed to the kernel that ran.  A static string owned by the library;
+ * NULL (with mla_last_error_message set) for an unsupported shape.  Host only. */
+const char* mla_decode_kernel_name(int s_q, int h_q, int h_kv, int kv_format);
+
 /* Bytes of the caller-owned decode workspace (split partials: fp32 partial
  * outputs and lse for at most batch + num_parts splits).  0 on bad input. */
 size_t mla_decode_workspace_size(int batch, int s_q, int h_q, int num_parts);

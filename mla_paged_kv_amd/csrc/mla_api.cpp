@@ -225,6 +225,16 @@ int mla_decode_num_parts(int batch, int s_q, int h_q, int h_kv, int kv_format, i
   return mla_plan_num_parts(batch, s_q, h_q, h_kv, kv_format, cus, wgs, num_parts_out);
 }
 
+const char* mla_decode_kernel_name(int s_q, int h_q, int h_kv, int kv_format) {
+  if (check_shape(1, s_q, h_q, h_kv, kv_format)) return nullptr;
+  const int kind = kv_format == MLA_KV_FP8_PACKED    ? mla::kDecodeFp8Packed
+                   : kv_format == MLA_KV_FP8_INDEXED ? mla::kDecodeFp8Indexed
+                   : kv_format == MLA_KV_FP16_PAGED  ? mla::kDecodeF16
+                                                     : mla::kDecodeBf16;
+  ok();
+  return mla::decode_kernel_name(s_q * h_q, h_kv, kind);
+}
+
 size_t mla_decode_workspace_size(int batch, int s_q, int h_q, int num_parts) {
   if (batch < 1 || s_q < 1 || h_q < 1 || num_parts < 1 || num_parts > MLA_MAX_PARTS || batch > MLA_MAX_BATCH) return 0;
   const size_t M = (size_t)s_q * h_q;

@@ -55,6 +55,7 @@ hipError_t decode_r128_occupancy(int kind, int* wgs_per_cu);
 hipError_t read_and_clear_error_flags_r128(int* flags);
 // Query rows one decode workgroup covers for this shape (either kernel family).
 int decode_rows_per_wg(int M, int h_kv, int kind);
+const char* decode_kernel_name(int M, int h_kv, int kind);
 
 hipError_t launch_sched(const int32_t* lengths, int batch, int num_parts, int32_t* meta, int32_t* num_splits,
                         hipStream_t stream, bool request_local = false);

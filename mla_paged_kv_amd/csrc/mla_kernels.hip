@@ -65,12 +65,14 @@ constexpr int kRowBytes = kDQK * 2;                 // 1152
 constexpr int kTileBytes = kTK * kRowBytes;         // 36864
 constexpr int kChunksPerRow = kRowBytes / 16;       // 72
 constexpr int kLoadsPerWave = kTileBytes / 1024 / 4;  // 9 wave-wide 16-B loads per tile per wave
-// P row pitch (bytes).  Measured on gfx950: 16-B reads of 16 rows at a 64-, 80-
-// or 144-B pitch run at half rate (bank conflicts), at 96 B at full rate.
-constexpr int kPStride = kTK * 2 + 32;
-constexpr int kRawTileBytes = 24 * 1024;            // FP8 raw tile slot (32 x 656 = 20992 B used)
-constexpr int kRawLoadsPerWave = 6;                 // 24 wave-wide loads per raw tile
-constexpr int kRawChunks = kTK * kRecBytes / 16;    // 1312
+// P row pitch (bytes) of the bf16 kernel, from SQ_LDS_BANK_CONFLICT on gfx950
+// probes of its exact access patterns: the 16-B reads of 16 rows (+16 B per
+// lane group) are conflict-free at a 96-B pitch (2-way at 80), the 8-B writes
+// 4-way (2-way at 80); P is read as often as it is written, so both cost the
+// same, and the reads are the ones on the PV waves' critical path.
+constexpr int kPStride = 96;
+constexpr int kRawTileBytes = kTK * kRecBytes;      // FP8 raw tile slot: 32 records, 20992 B
+constexpr int kRawChunks = kTK * kRecBytes / 16;    // 1312 16-B chunks = 20.5 wave-wide loads
 constexpr float kRescaleThreshold = 8.0f;           // log2 units: p <= 2^8 between rescales
 
 // LDS layout
@@ -504,24 +506,25 @@ struct TileLoader<false> {
   }
 };
 
-// FP8 packed workspace: tile = 32 consecutive 656-byte records of one query row.
+// FP8 packed workspace: tile = 32 consecutive 656-byte records of one query row
+// (1312 16-B chunks).  Wave w moves chunks [64 q, 64 q + 64) for q = w + 4 k,
+// k < 5 (the first 1280), and wave 0 also the last 32 (q = 20, lanes 0..31):
+// 6 loads for wave 0, 5 for the others (loads_in_flight).
 template <>
 struct TileLoader<true> {
-  uint32_t off[kRawLoadsPerWave];
-  __device__ void init(int w, int l) {
-#pragma unroll
-    for (int k = 0; k < kRawLoadsPerWave; ++k) {
-      int p = (w + 4 * k) * 64 + l;  // 16-B chunk position in the raw slot (0..1535)
-      // positions past the 1312 real chunks re-read chunk 0 (keeps every wave's
-      // load count uniform for the vmcnt bookkeeping; lands in unused LDS)
-      off[k] = (uint32_t)((p < kRawChunks ? p : 0) * 16);
-    }
-  }
+  static constexpr int kLoads = 6;  // at most, per wave
+  __device__ void init(int, int) {}
+  __device__ static int loads_of_wave(int w) { return w == 0 ? 6 : 5; }
   __device__ void issue(const DecodeArgs& a, int r, int key0, LDS_AS uint8_t* smem, int st, int w) {
-    const uint8_t* src = a.kv + ((int64_t)r * a.cap + key0) * kRecBytes;
+    const uint64_t src = uniform_u64((uint64_t)(uintptr_t)(a.kv + ((int64_t)r * a.cap + key0) * kRecBytes));
     LDS_AS uint8_t* dst = smem + kOffRaw + st * kRawTileBytes;
+    const uint32_t l = threadIdx.x & 63;
 #pragma unroll
-    for (int k = 0; k < kRawLoadsPerWave; ++k) load_lds16(src + off[k], dst + (w + 4 * k) * 1024);
+    for (int k = 0; k < 5; ++k) {
+      const int q = w + 4 * k;
+      load_lds16_s(src, (uint32_t)(q * 64 * 16) + 16u * l, dst + q * 1024);
+    }
+    if (w == 0 && l < (uint32_t)(kRawChunks - 20 * 64)) load_lds16_s(src, 20u * 64 * 16 + 16u * l, dst + 20 * 1024);
   }
 };
 
@@ -537,8 +540,10 @@ struct TileLoader<true> {
 // valid prefix outside the pool is flagged and replaced by 0.
 constexpr int kIdxLoadsPerWave = kTK / 4;  // 8
 struct IndexedLoader {
+  static constexpr int kLoads = kIdxLoadsPerWave;
   int n = 0;
   __device__ void init(int, int) {}
+  __device__ static int loads_of_wave(int) { return kIdxLoadsPerWave; }
   __device__ void issue(const DecodeArgs& a, int row, int key0, LDS_AS uint8_t* smem, int st, int w) const {
     const int l = threadIdx.x & 63;
     const int64_t limit = a.num_pages * kPage;
@@ -1086,30 +1091,41 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
 
 // ------------------------------------------------------------------ FP8 decode, wave-specialised
 //
-// The sparse FP8 paths with the two-role structure of decode_ws_kernel, and no
-// widened copy of the tile: the raw 656-byte records stay in the ring and the
-// E4M3 bytes are converted to bf16 in registers on their way to the MFMAs
-// (exact: every E4M3 value is a bf16 value).
-//   * QK waves 0..3 (16 rows each): K fragments are 8 E4M3 bytes per lane
-//     (ds_read_b64, four v_cvt_scalef32_pk_bf16_fp8 with scale 1); the RoPE
-//     k-steps read bf16 directly.  The four 128-dim NoPE blocks and the RoPE
-//     part accumulate apart, and each key's fp32 block scales combine them at
-//     the end of the tile.  The softmax of tile t-1 runs between the k-steps of
-//     tile t; P(t-1) is written four times, multiplied by each key's scale of
-//     NoPE block b for the PV waves of block b.  They also stream the ring.
+// The sparse FP8 paths with the two-role structure of decode_ws_kernel.  The raw
+// 656-byte records stream into a ring; E4M3 values are converted to bf16
+// exactly (every E4M3 value is a bf16 value) and the per-key fp32 block scales
+// are applied in fp32 to the scores and to P, never to a rounded K or V.
+//   * Each tile's NoPE K is converted once, into a shared bf16 buffer: at the
+//     start of iteration t each QK wave converts a quarter of raw tile t (and
+//     zeroes the NoPE bytes of its records past the valid count, which the PV
+//     waves read next iteration), then every wave passes a barrier.
+//   * QK waves 0..3 (16 rows each) then compute S(t)^T = K(t) Q^T like the bf16
+//     kernel, K operands from the converted buffer (NoPE) and the raw records
+//     (RoPE, already bf16).  The four 128-dim NoPE blocks and the RoPE part
+//     accumulate apart, and each key's block scales combine them at the end of
+//     the tile.  The softmax of tile t-1 runs between the k-steps of tile t;
+//     P(t-1) is written four times, multiplied by each key's scale of NoPE
+//     block b for the PV waves of block b.  They also stream the ring.
 //   * PV waves 4..7: wave 4+w owns output columns [128w, 128w+128) -- NoPE
-//     block w -- for all rows.  V^T fragments come from ds_read_b64_tr_b8 (in a
-//     16-lane group, lane j addresses key 8g + j/2 at byte 8 (j & 1) of the 16
-//     columns; lane i receives column i of keys 8g .. 8g+7), converted like K.
-// One barrier per tile; the ring holds 4 raw tiles (2 in flight), as in the
+//     block w -- for all rows.  V^T fragments come from ds_read_b64_tr_b8 on the
+//     raw records (in a 16-lane group, lane j addresses key 8g + j/2 at byte
+//     8 (j & 1) of the 16 columns; lane i receives column i of keys 8g ..
+//     8g+7), converted in registers.  Half of their MFMAs run before the
+//     conversion barrier, half after.
+// Two barriers per tile; the ring holds 4 raw tiles (2 in flight), as in the
 // bf16 kernel.  64 rows per workgroup (h_q is 64 or 128 on these paths).
-constexpr int kF8OffP = kStages * kRawTileBytes;                         // 98304: P[2 parities][4 blocks]
-constexpr int kF8OffAlpha = kF8OffP + 2 * 4 * kPBufBytes;                // 147456
-constexpr int kF8OffFlag = kF8OffAlpha + 2 * kMaxRowsPerWG * 4;          // 147968
-constexpr int kF8OffL = kF8OffFlag + 64;                                 // 148032
-constexpr int kF8LdsBytes = kF8OffL + kMaxRowsPerWG * 4;                 // 148288
+constexpr int kCvtPitch = 1024 + 32;  // converted NoPE row: 512 bf16 + 32 B (16-row reads conflict-free)
+constexpr int kF8PPitch = kTK * 4 + 16;  // fp32 P row: 32 keys + 16 B
+constexpr int kF8PBuf = kMaxRowsPerWG * kF8PPitch;                       // 9216
+constexpr int kF8OffC = kStages * kRawTileBytes;                         // 83968: converted NoPE K, 32 rows
+constexpr int kF8OffP = kF8OffC + kTK * kCvtPitch;                       // 117760: fp32 P[2 parities]
+constexpr int kF8OffS = kF8OffP + 2 * kF8PBuf;                           // 136192: block scales [4 tiles][4][32]
+constexpr int kF8OffAlpha = kF8OffS + kStages * 4 * kTK * 4;             // 138240
+constexpr int kF8OffFlag = kF8OffAlpha + 2 * kMaxRowsPerWG * 4;          // 138752
+constexpr int kF8OffL = kF8OffFlag + 64;                                 // 138816
+constexpr int kF8LdsBytes = kF8OffL + kMaxRowsPerWG * 4;                 // 139072
 static_assert(kF8LdsBytes <= 160 * 1024, "FP8 wave-specialised LDS budget");
-constexpr int kF8QkDepth = 3;  // raw K fragment ring depth
+static_assert(kF8OffC % 16 == 0 && kF8OffP % 16 == 0 && kF8OffS % 16 == 0, "16-B aligned LDS regions");
 
 // 8 E4M3 bytes (two dwords, byte k = element k) -> 8 bf16, exactly
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 raw) {
@@ -1121,22 +1137,6 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 raw) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// Zero the 512 NoPE bytes (the V part) of records [nvalid, 32) of a raw FP8
-// tile; `tid` in [0, 256) strides by 256.  Keys past the valid count score -inf
-// and get P = 0, but 0 * NaN would still poison PV if such a record's bytes
-// decode to NaN (the by-index loader reads record 0 for them).
-__device__ __forceinline__ void zero_tail_records_256(LDS_AS uint8_t* raw, int nvalid, int tid) {
-  const int n = (kTK - nvalid) * (512 / 16);
-  for (int idx = tid; idx < n; idx += 256) {
-    const int kr = nvalid + (idx >> 5);
-    *reinterpret_cast<LDS_AS u32x4*>(raw + kr * kRecBytes + 16 * (idx & 31)) = u32x4{0u, 0u, 0u, 0u};
-  }
-}
-
-__device__ __forceinline__ u32x2 lds_read_b64(const LDS_AS uint8_t* p) {
-  return *reinterpret_cast<const LDS_AS u32x2*>(p);
-}
-
 __device__ __forceinline__ u32x2 lds_read_tr8(const LDS_AS uint8_t* p) {
   typedef int i32x2_t __attribute__((ext_vector_type(2)));
   const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
@@ -1144,12 +1144,43 @@ __device__ __forceinline__ u32x2 lds_read_tr8(const LDS_AS uint8_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Converts the NoPE bytes of keys [8w, 8w + 8) of a raw tile into the bf16
+// buffer (row k at k * kCvtPitch), copies their four block scales into the
+// tile's scale table (scale b of key k at 32 b + k), and zeroes, in the raw
+// tile, the NoPE bytes of those keys at or past `nvalid`: they score -inf and
+// get P = 0, but 0 * NaN would still poison PV if such a record decodes to NaN
+// (the by-index loader reads record 0 for them).  Lane l handles 8-byte units
+// (l & 7) + 8 j, j < 8, of key 8w + (l >> 3): each group of 8 lanes writes 128
+// contiguous bytes.
+__device__ __forceinline__ void convert_nope_quarter(LDS_AS uint8_t* raw, LDS_AS uint8_t* cvt, LDS_AS float* scales,
+                                                     int w, int nvalid) {
+  const int l = threadIdx.x & 63;
+  const int key = 8 * w + (l >> 3);
+  LDS_AS uint8_t* src = raw + key * kRecBytes + 8 * (l & 7);
+  LDS_AS uint8_t* dst = cvt + key * kCvtPitch + 16 * (l & 7);
+  u32x2 v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const LDS_AS u32x2*>(src + 64 * j);
+  float sc = 0.f;
+  const int skey = 8 * w + ((l >> 2) & 7), sb = l & 3;
+  if (l < 32) sc = *reinterpret_cast<const LDS_AS float*>(raw + skey * kRecBytes + 512 + 4 * sb);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) *reinterpret_cast<LDS_AS bf16x8*>(dst + 128 * j) = e4m3x8_to_bf16(v[j]);
+  if (l < 32) scales[32 * sb + skey] = sc;
+  if (nvalid < kTK && key >= nvalid) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) *reinterpret_cast<LDS_AS u32x2*>(src + 64 * j) = u32x2{0u, 0u};
+  }
+}
+
 template <bool IDX>
 __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs a) {
   constexpr int RB = 4, MB = 64;
-  constexpr int LPW = IDX ? kIdxLoadsPerWave : kRawLoadsPerWave;
+  using Loader = std::conditional_t<IDX, IndexedLoader, TileLoader<true>>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[kF8LdsBytes];
   LDS_AS uint8_t* smem = (LDS_AS uint8_t*)(smem_raw);
+  LDS_AS uint8_t* cvt = smem + kF8OffC;
+  LDS_AS float* scales_s = reinterpret_cast<LDS_AS float*>(smem + kF8OffS);     // [4 tiles][4 blocks][32 keys]
   LDS_AS float* alpha_s = reinterpret_cast<LDS_AS float*>(smem + kF8OffAlpha);  // [2][64]
   LDS_AS uint8_t* flag_s = smem + kF8OffFlag;                                    // [2][4] bytes
   LDS_AS float* l_s = reinterpret_cast<LDS_AS float*>(smem + kF8OffL);
@@ -1171,8 +1202,19 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
     return;
   }
 
-  std::conditional_t<IDX, IndexedLoader, TileLoader<true>> loader;
+  Loader loader;
   loader.init(w, l);  // used by the QK waves
+  // loads of the tile in flight that a QK wave may leave outstanding while it
+  // waits for the next one (wave-uniform)
+  const bool wave0 = w == 0;
+  auto wait_all_but_inflight = [&]() {
+    if constexpr (IDX) {
+      wait_vmcnt<kIdxLoadsPerWave>();
+    } else {
+      if (wave0) wait_vmcnt<6>();
+      else wait_vmcnt<5>();
+    }
+  };
   const int row_local = 16 * w + li;
   // PV: lane j of 16-lane group g addresses key 8g + j/2, column half j & 1
   const int tr8_key = 8 * g + (li >> 1);
@@ -1202,7 +1244,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
       continue;
     }
     const int rho = rbk * MB + row_local;
-    auto raw_slot = [&](int t) -> const LDS_AS uint8_t* { return smem + kOffRaw + (t & 3) * kRawTileBytes; };
+    auto raw_slot = [&](int t) -> LDS_AS uint8_t* { return smem + kOffRaw + (t & 3) * kRawTileBytes; };
 
     if (is_qk) {
       // ================================================================ QK waves
@@ -1256,31 +1298,15 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
             psum = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
             lpart = lpart * alpha + psum;
             break;
-          case 11:
-          case 12:
-          case 13:
-          case 14: {
-            // P of NoPE block b = step - 11: p times each key's scale b
-            const int b = step - 11;
-            const LDS_AS uint8_t* rawt = raw_slot(ts);
-            const int nvalid = min(kTK, t1 - (t0 + ts * kTK));
-            float sc[8];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int kr = 16 * kb + 4 * g + i;
-                sc[kb * 4 + i] = kr < nvalid ? *reinterpret_cast<const LDS_AS float*>(rawt + kr * kRecBytes + 512 + 4 * b)
-                                             : 0.f;
-              }
-            LDS_AS uint8_t* prow = smem + kF8OffP + ((ts & 1) * 4 + b) * kPBufBytes + row_local * kPStride + 8 * g;
-            *reinterpret_cast<LDS_AS u32x2*>(prow) =
-                u32x2{pack_bf16x2(pv[0] * sc[0], pv[1] * sc[1]), pack_bf16x2(pv[2] * sc[2], pv[3] * sc[3])};
-            *reinterpret_cast<LDS_AS u32x2*>(prow + 32) =
-                u32x2{pack_bf16x2(pv[4] * sc[4], pv[5] * sc[5]), pack_bf16x2(pv[6] * sc[6], pv[7] * sc[7])};
+          case 11: {
+            // unnormalised P of tile ts in fp32 (keys 4g + i and 16 + 4g + i); the
+            // PV wave of NoPE block b multiplies it by each key's scale b
+            LDS_AS uint8_t* prow = smem + kF8OffP + (ts & 1) * kF8PBuf + row_local * kF8PPitch + 16 * g;
+            *reinterpret_cast<LDS_AS f32x4*>(prow) = f32x4{pv[0], pv[1], pv[2], pv[3]};
+            *reinterpret_cast<LDS_AS f32x4*>(prow + 64) = f32x4{pv[4], pv[5], pv[6], pv[7]};
             break;
           }
-          case 15: {
+          case 12: {
             const bool any = __any(upd);
             if (any && g == 0) alpha_s[(ts & 1) * kMaxRowsPerWG + row_local] = alpha;
             if (l == 0) flag_s[(ts & 1) * 4 + w] = any ? 1 : 0;
@@ -1290,43 +1316,39 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
         }
       };
 
-      // QK^T of tile t (raw slot), scores combined with the block scales -> sx
+      // QK^T of tile t: NoPE k-steps (s < 16) from the converted buffer (key
+      // 16 kb + li at kb * 16 * kCvtPitch + li * kCvtPitch, dims 32 s + 8 g ..),
+      // RoPE k-steps from the raw records; scores combined with the block scales
+      // -> sx
       auto qk = [&](int t, auto hook) {
         const LDS_AS uint8_t* rawt = raw_slot(t);
-        const LDS_AS uint8_t* kr0p = rawt + li * kRecBytes + 8 * g;         // keys li (kb 0)
-        const LDS_AS uint8_t* kr1p = rawt + (16 + li) * kRecBytes + 8 * g;  // keys 16 + li (kb 1)
+        const LDS_AS uint8_t* c0 = cvt + li * kCvtPitch + 16 * g;
+        const LDS_AS uint8_t* c1 = c0 + 16 * kCvtPitch;
+        const LDS_AS uint8_t* r0 = rawt + li * kRecBytes + 528 + 16 * g;
+        const LDS_AS uint8_t* r1 = r0 + 16 * kRecBytes;
+        auto rd0 = [&](int s) { return lds_read_b128(s < 16 ? c0 + 64 * s : r0 + 64 * (s - 16)); };
+        auto rd1 = [&](int s) { return lds_read_b128(s < 16 ? c1 + 64 * s : r1 + 64 * (s - 16)); };
+        constexpr int D = kQkDepth;
         f32x4 acc[2][5];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int gi = 0; gi < 5; ++gi) acc[kb][gi] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // operand of k-step s: NoPE (s < 16) 8 E4M3 bytes at 32s, RoPE 16 B of bf16
-        auto opnd = [&](const LDS_AS uint8_t* p, int s) -> bf16x8 {
-          if (s < 16) return e4m3x8_to_bf16(lds_read_b64(p + 32 * s));
-          return lds_read_b128(p - 8 * g + 528 + 64 * (s - 16) + 16 * g);
-        };
-        u32x2 rk0[kF8QkDepth], rk1[kF8QkDepth];
-        bf16x8 rp0[2], rp1[2];
+        bf16x8 k0[D], k1[D];
 #pragma unroll
-        for (int s = 0; s < kF8QkDepth - 1; ++s) {
-          rk0[s] = lds_read_b64(kr0p + 32 * s);
-          rk1[s] = lds_read_b64(kr1p + 32 * s);
+        for (int s = 0; s < D - 1; ++s) {
+          k0[s] = rd0(s);
+          k1[s] = rd1(s);
         }
 #pragma unroll
         for (int s = 0; s < 18; ++s) {
-          const int sn = s + kF8QkDepth - 1;
-          if (sn < 16) {
-            rk0[sn % kF8QkDepth] = lds_read_b64(kr0p + 32 * sn);
-            rk1[sn % kF8QkDepth] = lds_read_b64(kr1p + 32 * sn);
-          } else if (sn < 18) {
-            rp0[sn - 16] = opnd(kr0p, sn);
-            rp1[sn - 16] = opnd(kr1p, sn);
+          if (s + D - 1 < 18) {
+            k0[(s + D - 1) % D] = rd0(s + D - 1);
+            k1[(s + D - 1) % D] = rd1(s + D - 1);
           }
           const int gi = s < 16 ? (s >> 2) : 4;
-          const bf16x8 k0 = s < 16 ? e4m3x8_to_bf16(rk0[s % kF8QkDepth]) : rp0[s - 16];
-          const bf16x8 k1 = s < 16 ? e4m3x8_to_bf16(rk1[s % kF8QkDepth]) : rp1[s - 16];
-          acc[0][gi] = mfma16(k0, qreg[s], acc[0][gi]);
-          acc[1][gi] = mfma16(k1, qreg[s], acc[1][gi]);
+          acc[0][gi] = mfma16(k0[s % D], qreg[s], acc[0][gi]);
+          acc[1][gi] = mfma16(k1[s % D], qreg[s], acc[1][gi]);
           hook(s);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -1349,7 +1371,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
 
       if (ntile > 0) loader.issue(a, lrow, t0, smem, 0, w);
       if (ntile > 1) loader.issue(a, lrow, t0 + kTK, smem, 1, w);
-      if (ntile > 1) wait_vmcnt<LPW>();
+      if (ntile > 1) wait_all_but_inflight();
       else wait_vmcnt<0>();
       sync_lds();  // tile 0 resident
       auto iter = [&](auto do_qk_c, auto do_sm_c, int t) {
@@ -1357,6 +1379,9 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
         constexpr bool DO_SM = decltype(do_sm_c)::value;
         const bool more = t + 2 < ntile;
         if (more) loader.issue(a, lrow, t0 + (t + 2) * kTK, smem, (t + 2) & 3, w);
+        if constexpr (DO_QK)
+          convert_nope_quarter(raw_slot(t), cvt, scales_s + (t & 3) * 4 * kTK, w, min(kTK, t1 - (t0 + t * kTK)));
+        sync_lds();  // tile t's NoPE K converted
         if constexpr (DO_QK) {
           if constexpr (DO_SM) {
             // the softmax of t-1 reads sx, which qk(t) overwrites only at its end
@@ -1366,7 +1391,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
           }
         } else if constexpr (DO_SM) {
 #pragma unroll
-          for (int step = 0; step < 16; ++step) softmax_step(step, t - 1);
+          for (int step = 0; step < 13; ++step) softmax_step(step, t - 1);
         }
         if (t == ntile) {  // every tile's softmax is done: row sums for the output stage
           const float lt = row4_sum(lpart);
@@ -1380,7 +1405,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
           }
         }
         if (t + 1 < ntile) {
-          if (more) wait_vmcnt<LPW>();
+          if (more) wait_all_but_inflight();
           else wait_vmcnt<0>();
         }
         sync_lds();
@@ -1407,24 +1432,33 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
         v[db] = lds_read_tr8(raw_slot(t) + tr8_key * kRecBytes + 128 * w + 16 * db + tr8_col);
       };
       sync_lds();  // tile 0 resident
+      // one iteration: PV(t-2) from registers, V(t-1) into registers; the
+      // conversion barrier of the QK waves falls after the first four 16-column
+      // blocks
       auto iter = [&](auto do_pv_c, auto do_vread_c, int t) {
         constexpr bool DO_PV = decltype(do_pv_c)::value;
         constexpr bool DO_VREAD = decltype(do_vread_c)::value;
-        if (t < ntile) {  // tile t is resident; its V is read in iteration t + 1
-          const int nvalid = min(kTK, t1 - (t0 + t * kTK));
-          if (nvalid < kTK) zero_tail_records_256(smem + kOffRaw + (t & 3) * kRawTileBytes, nvalid, 64 * w + l);
-        }
         const int tp = t - 2;
         uint32_t fl = 0;
         float al[RB];
         bf16x8 bp[RB];
         if constexpr (DO_PV) {
-          const LDS_AS uint8_t* pb = smem + kF8OffP + ((tp & 1) * 4 + w) * kPBufBytes;
+          // P^T operand of row 16 rb + li: keys 8g .. 8g+7 of P(t-2) times their scale w
+          const LDS_AS uint8_t* pb = smem + kF8OffP + (tp & 1) * kF8PBuf + li * kF8PPitch + 32 * g;
+          const LDS_AS float* sp = scales_s + (tp & 3) * 4 * kTK + kTK * w + 8 * g;
+          const f32x4 s0 = *reinterpret_cast<const LDS_AS f32x4*>(sp);
+          const f32x4 s1 = *reinterpret_cast<const LDS_AS f32x4*>(sp + 4);
           fl = *reinterpret_cast<const LDS_AS uint32_t*>(flag_s + (tp & 1) * 4);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) al[rb] = alpha_s[(tp & 1) * kMaxRowsPerWG + 16 * rb + li];
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) bp[rb] = lds_read_b128(pb + (16 * rb + li) * kPStride + 16 * g);
+          for (int rb = 0; rb < RB; ++rb) {
+            const f32x4 p0 = *reinterpret_cast<const LDS_AS f32x4*>(pb + 16 * rb * kF8PPitch);
+            const f32x4 p1 = *reinterpret_cast<const LDS_AS f32x4*>(pb + 16 * rb * kF8PPitch + 16);
+            bp[rb] = __builtin_bit_cast(
+                bf16x8, u32x4{pack_bf16x2(p0[0] * s0[0], p0[1] * s0[1]), pack_bf16x2(p0[2] * s0[2], p0[3] * s0[3]),
+                              pack_bf16x2(p1[0] * s1[0], p1[1] * s1[1]), pack_bf16x2(p1[2] * s1[2], p1[3] * s1[3])});
+          }
           if (tp > 0) {
             const uint32_t fls = __builtin_amdgcn_readfirstlane(fl);
 #pragma unroll
@@ -1435,18 +1469,22 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
               }
             }
           }
+        }
+        auto blocks = [&](int db0) {
 #pragma unroll
-          for (int db = 0; db < 8; ++db) {
-            const bf16x8 av = e4m3x8_to_bf16(v[db]);
+          for (int db = db0; db < db0 + 4; ++db) {
+            if constexpr (DO_PV) {
+              const bf16x8 av = e4m3x8_to_bf16(v[db]);
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) o[db][rb] = mfma16(av, bp[rb], o[db][rb]);
+              for (int rb = 0; rb < RB; ++rb) o[db][rb] = mfma16(av, bp[rb], o[db][rb]);
+            }
             if constexpr (DO_VREAD) vread(t - 1, db);
             __builtin_amdgcn_sched_barrier(0);
           }
-        } else if constexpr (DO_VREAD) {
-#pragma unroll
-          for (int db = 0; db < 8; ++db) vread(t - 1, db);
-        }
+        };
+        blocks(0);
+        sync_lds();  // the QK waves' conversion barrier
+        blocks(4);
         sync_lds();
       };
       using F = std::false_type;
@@ -1522,6 +1560,23 @@ static hipError_t launch_decode_t(const DecodeArgs& a, int kind, hipStream_t str
 int decode_rows_per_wg(int M, int h_kv, int kind) {
   if (decode_r128_shape(M, h_kv, kind)) return 128;
   return 16 * decode_row_blocks_per_wg(h_kv > 1 ? M / h_kv : M);
+}
+
+// Name of the instantiation launch_decode runs for this shape (as profilers
+// print it, without namespaces and parameter list).
+const char* decode_kernel_name(int M, int h_kv, int kind) {
+  if (decode_r128_shape(M, h_kv, kind)) return kind == kDecodeF16 ? "decode_r128_kernel<true>" : "decode_r128_kernel<false>";
+  if (kind == kDecodeFp8Packed) return "decode_fp8ws_kernel<false>";
+  if (kind == kDecodeFp8Indexed) return "decode_fp8ws_kernel<true>";
+  static const char* const names[3][2][2] = {
+      {{"decode_ws_kernel<1, false, false>", "decode_ws_kernel<1, false, true>"},
+       {"decode_ws_kernel<1, true, false>", "decode_ws_kernel<1, true, true>"}},
+      {{"decode_ws_kernel<2, false, false>", "decode_ws_kernel<2, false, true>"},
+       {"decode_ws_kernel<2, true, false>", "decode_ws_kernel<2, true, true>"}},
+      {{"decode_ws_kernel<4, false, false>", "decode_ws_kernel<4, false, true>"},
+       {"decode_ws_kernel<4, true, false>", "decode_ws_kernel<4, true, true>"}}};
+  const int rb = decode_row_blocks_per_wg(h_kv > 1 ? M / h_kv : M);
+  return names[rb == 1 ? 0 : rb == 2 ? 1 : 2][kind == kDecodeF16 ? 1 : 0][h_kv > 1 ? 1 : 0];
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int kind, hipStream_t stream) {

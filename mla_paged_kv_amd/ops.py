@@ -47,6 +47,7 @@ _SIGS = {
     "mla_last_error_message": ([], ctypes.c_char_p),
     "mla_decode_num_parts": ([_i32, _i32, _i32, _i32, _i32, _P], _i32),
     "mla_plan_num_parts": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32, _P], _i32),
+    "mla_decode_kernel_name": ([_i32, _i32, _i32, _i32], ctypes.c_char_p),
     "mla_decode_workspace_size": ([_i32, _i32, _i32, _i32], _sz),
     "mla_packed_kv_workspace_size": ([_i32, _i32, _i32], _sz),
     "mla_get_decode_metadata": ([_P, _i32, _i32, _i32, _i32, _i32, _P, _P, _P], _i32),
@@ -88,6 +89,35 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+class BoundCall:
+    """One entry point with its arguments checked and converted once.
+
+    Calling it only crosses the C ABI: no tensor checks, no conversions.  For
+    loops that issue the same launch many times (timed loops, a serving loop
+    whose buffers stay put).  It keeps the tensors it points into alive; the
+    stream is the one current when it was bound."""
+
+    __slots__ = ("name", "_fn", "_args", "_keep")
+
+    def __init__(self, name, args, keep):
+        self.name = name
+        self._fn = getattr(_lib, name)
+        self._args = tuple(a if isinstance(a, t) or a is None else t(a) for a, t in zip(args, self._fn.argtypes))
+        self._keep = tuple(keep)
+
+    def __call__(self):
+        status = self._fn(*self._args)
+        if status != MLA_OK:
+            raise MLAError(status, mla_last_error_message())
+
+
+def _call(name, args, bind, keep=()):
+    if bind:
+        return BoundCall(name, args, keep)
+    _check(getattr(_lib, name)(*args))
+    return None
+
+
 def _stream(stream=None):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -121,6 +151,13 @@ def mla_plan_num_parts(batch, s_q, h_q, kv_format, cus, wgs_per_cu, h_kv=1) -> i
     return out.value
 
 
+def mla_decode_kernel_name(s_q, h_q, h_kv=1, kv_format=KV_BF16_PAGED) -> str:
+    name = _lib.mla_decode_kernel_name(s_q, h_q, h_kv, kv_format)
+    if name is None:
+        raise MLAError(MLA_ERR_UNSUPPORTED, mla_last_error_message())
+    return name.decode()
+
+
 def mla_decode_workspace_size(batch, s_q, h_q, num_parts) -> int:
     return int(_lib.mla_decode_workspace_size(batch, s_q, h_q, num_parts))
 
@@ -130,7 +167,9 @@ def mla_packed_kv_workspace_size(batch, s_q, topk_capacity) -> int:
 
 
 def mla_get_decode_metadata(seqlens, batch, s_q, h_q, h_kv, num_parts, sched_meta=None, num_splits=None,
-                            stream=None):
+                            stream=None, bind=False):
+    """Scheduler metadata into (sched_meta, num_splits), allocated here if None.
+    With bind=True the launch is not made: a BoundCall that makes it is returned."""
     _need(seqlens, "seqlens", torch.int32, (batch,))
     dev = seqlens.device
     if sched_meta is None:
@@ -139,9 +178,10 @@ def mla_get_decode_metadata(seqlens, batch, s_q, h_q, h_kv, num_parts, sched_met
         num_splits = torch.empty((batch + 1,), dtype=torch.int32, device=dev)
     _need(sched_meta, "sched_meta", torch.int32, (num_parts, SCHED_META_INTS))
     _need(num_splits, "num_splits", torch.int32, (batch + 1,))
-    _check(_lib.mla_get_decode_metadata(_ptr(seqlens), batch, s_q, h_q, h_kv, num_parts, _ptr(sched_meta),
-                                        _ptr(num_splits), _stream(stream)))
-    return sched_meta, num_splits
+    bound = _call("mla_get_decode_metadata", (_ptr(seqlens), batch, s_q, h_q, h_kv, num_parts, _ptr(sched_meta),
+                                              _ptr(num_splits), _stream(stream)), bind,
+                  (seqlens, sched_meta, num_splits))
+    return bound if bind else (sched_meta, num_splits)
 
 
 def _act_dtype(kv_format):
@@ -149,7 +189,7 @@ def _act_dtype(kv_format):
 
 
 def mla_get_packed_decode_metadata(topk_length, batch, s_q, h_q, topk_capacity, num_parts, policy=SCHED_AUTO,
-                                   sched_meta=None, num_splits=None, stream=None):
+                                   sched_meta=None, num_splits=None, stream=None, bind=False):
     _need(topk_length, "topk_length", torch.int32, (batch,))
     dev = topk_length.device
     if sched_meta is None:
@@ -158,9 +198,10 @@ def mla_get_packed_decode_metadata(topk_length, batch, s_q, h_q, topk_capacity, 
         num_splits = torch.empty((batch + 1,), dtype=torch.int32, device=dev)
     _need(sched_meta, "sched_meta", torch.int32, (num_parts, SCHED_META_INTS))
     _need(num_splits, "num_splits", torch.int32, (batch + 1,))
-    _check(_lib.mla_get_packed_decode_metadata(_ptr(topk_length), batch, s_q, h_q, topk_capacity, num_parts, policy,
-                                               _ptr(sched_meta), _ptr(num_splits), _stream(stream)))
-    return sched_meta, num_splits
+    bound = _call("mla_get_packed_decode_metadata", (_ptr(topk_length), batch, s_q, h_q, topk_capacity, num_parts,
+                                                     policy, _ptr(sched_meta), _ptr(num_splits), _stream(stream)),
+                  bind, (topk_length, sched_meta, num_splits))
+    return bound if bind else (sched_meta, num_splits)
 
 
 def _decode_args(q, kv, kv_format, block_table, seqlens, sched_meta, num_splits, out, lse, topk_capacity):
@@ -204,15 +245,18 @@ def _decode_args(q, kv, kv_format, block_table, seqlens, sched_meta, num_splits,
 
 
 def mla_decode_fwd(q, kv, kv_format, block_table, seqlens, softmax_scale, causal, sched_meta, num_splits, out, lse,
-                   workspace, topk_capacity=0, stream=None):
+                   workspace, topk_capacity=0, stream=None, bind=False):
+    """Decode into out/lse (unsplit requests) and the workspace's partials.  With
+    bind=True a BoundCall that makes the launch is returned instead."""
     args = _decode_args(q, kv, kv_format, block_table, seqlens, sched_meta, num_splits, out, lse, topk_capacity)
     b, s_q, h_q, h_kv, num_pages, max_pages, topk_capacity = args
     _need(workspace, "workspace", torch.uint8)
-    _check(_lib.mla_decode_fwd(
+    return _call("mla_decode_fwd", (
         _ptr(q), _ptr(kv), kv_format, num_pages, _ptr(block_table) if kv_format != KV_FP8_PACKED else None,
         max_pages, _ptr(seqlens), topk_capacity, b, s_q, h_q, h_kv, float(softmax_scale), int(bool(causal)),
         _ptr(sched_meta), _ptr(num_splits), sched_meta.shape[0], _ptr(out), _ptr(lse), _ptr(workspace),
-        workspace.numel(), _stream(stream)))
+        workspace.numel(), _stream(stream)), bind, (q, kv, block_table, seqlens, sched_meta, num_splits, out, lse,
+                                                     workspace))
 
 
 def mla_decode_fwd_noalloc(q, kv, kv_format, block_table, seqlens, softmax_scale, causal, sched_meta, num_splits,
@@ -227,16 +271,20 @@ def mla_decode_fwd_noalloc(q, kv, kv_format, block_table, seqlens, softmax_scale
         _ptr(sched_meta), _ptr(num_splits), sched_meta.shape[0], _ptr(out), _ptr(lse), _stream(stream)))
 
 
-def mla_combine(num_splits, workspace, batch, s_q, h_q, num_parts, out, lse, stream=None, kv_format=KV_BF16_PAGED):
+def mla_combine(num_splits, workspace, batch, s_q, h_q, num_parts, out, lse, stream=None, kv_format=KV_BF16_PAGED,
+                bind=False):
+    """Merge the split partials into out/lse.  With bind=True a BoundCall that
+    makes the launch is returned instead."""
     _need(num_splits, "num_splits", torch.int32, (batch + 1,))
     _need(workspace, "workspace", torch.uint8)
     _need(out, "out", _act_dtype(kv_format), (batch, s_q, h_q, D_V))
     _need(lse, "lse", torch.float32, (batch, s_q, h_q))
-    _check(_lib.mla_combine(_ptr(num_splits), _ptr(workspace), workspace.numel(), batch, s_q, h_q, num_parts,
-                            kv_format, _ptr(out), _ptr(lse), _stream(stream)))
+    return _call("mla_combine", (_ptr(num_splits), _ptr(workspace), workspace.numel(), batch, s_q, h_q, num_parts,
+                                 kv_format, _ptr(out), _ptr(lse), _stream(stream)), bind,
+                 (num_splits, workspace, out, lse))
 
 
-def mla_pack_selected_kv(kcache_fp8, indices, topk_length, workspace=None, stream=None):
+def mla_pack_selected_kv(kcache_fp8, indices, topk_length, workspace=None, stream=None, bind=False):
     _need(kcache_fp8, "kcache_fp8", torch.uint8)
     if tuple(kcache_fp8.shape[1:]) != (PAGE, 1, REC_BYTES):
         raise ValueError(f"kcache_fp8 shape {tuple(kcache_fp8.shape)}, expected [pages, 64, 1, 656]")
@@ -247,9 +295,10 @@ def mla_pack_selected_kv(kcache_fp8, indices, topk_length, workspace=None, strea
     if workspace is None:
         workspace = torch.empty((nbytes,), dtype=torch.uint8, device=indices.device)
     _need(workspace, "workspace", torch.uint8)
-    _check(_lib.mla_pack_selected_kv(_ptr(kcache_fp8), kcache_fp8.shape[0], _ptr(indices), _ptr(topk_length), b,
-                                     s_q, cap, _ptr(workspace), workspace.numel(), _stream(stream)))
-    return workspace
+    bound = _call("mla_pack_selected_kv", (_ptr(kcache_fp8), kcache_fp8.shape[0], _ptr(indices), _ptr(topk_length),
+                                           b, s_q, cap, _ptr(workspace), workspace.numel(), _stream(stream)), bind,
+                  (kcache_fp8, indices, topk_length, workspace))
+    return bound if bind else workspace
 
 
 def mla_patch_packed_kv(kcache_fp8, indices, topk_length, new_ids, workspace, stream=None):

@@ -85,6 +85,25 @@ def test_plan_num_parts_multi_kv_head(batch, s_q, h_q, h_kv):
     assert ops.mla_plan_num_parts(batch, s_q, h_q, ops.KV_BF16_PAGED, 256, 1, h_kv=h_kv) == want
 
 
+@pytest.mark.parametrize("s_q,h_q,h_kv,fmt,name", [
+    (1, 128, 1, ops.KV_BF16_PAGED, "decode_ws_kernel<4, false, false>"),   # 128 rows: two 64-row workgroups
+    (1, 16, 1, ops.KV_BF16_PAGED, "decode_ws_kernel<1, false, false>"),
+    (1, 32, 1, ops.KV_FP16_PAGED, "decode_ws_kernel<2, true, false>"),
+    (2, 128, 1, ops.KV_BF16_PAGED, "decode_r128_kernel<false>"),          # 256 rows: the 128-row kernel
+    (4, 128, 1, ops.KV_FP16_PAGED, "decode_r128_kernel<true>"),
+    (2, 128, 2, ops.KV_BF16_PAGED, "decode_ws_kernel<4, false, true>"),    # several KV heads
+    (1, 64, 1, ops.KV_FP8_PACKED, "decode_fp8ws_kernel<false>"),
+    (16, 128, 1, ops.KV_FP8_INDEXED, "decode_fp8ws_kernel<true>"),
+])
+def test_decode_kernel_name(s_q, h_q, h_kv, fmt, name):
+    assert ops.mla_decode_kernel_name(s_q, h_q, h_kv, fmt) == name
+
+
+def test_decode_kernel_name_rejects_unsupported_shape():
+    with pytest.raises(ops.MLAError):
+        ops.mla_decode_kernel_name(1, 24, 1, ops.KV_BF16_PAGED)
+
+
 def decode_call(**kw):
     args = dict(q=FAKE, kv=FAKE, fmt=ops.KV_BF16_PAGED, num_pages=16, bt=FAKE, max_pages=4, seqlens=FAKE, cap=0,
                 batch=2, s_q=1, h_q=128, h_kv=1, scale=0.04, causal=0, meta=FAKE, ns=FAKE, parts=8, out=FAKE,
