@@ -47,13 +47,7 @@ struct DecodeArgs {
 // 16 * RB with RB in {1, 2, 4}.
 int decode_row_blocks_per_wg(int M);
 
-// The 128-row dense kernel (mla_decode_r128.hip): bf16 / fp16 pages, one KV
-// head, M a multiple of 128.  One workgroup per (part, 128-row block).
-bool decode_r128_shape(int M, int h_kv, int kind);
-hipError_t launch_decode_r128(const struct DecodeArgs& a, int kind, hipStream_t stream);
-hipError_t decode_r128_occupancy(int kind, int* wgs_per_cu);
-hipError_t read_and_clear_error_flags_r128(int* flags);
-// Query rows one decode workgroup covers for this shape (either kernel family).
+// Query rows one decode workgroup covers for this shape.
 int decode_rows_per_wg(int M, int h_kv, int kind);
 const char* decode_kernel_name(int M, int h_kv, int kind);
 

@@ -1558,14 +1558,13 @@ static hipError_t launch_decode_t(const DecodeArgs& a, int kind, hipStream_t str
 }
 
 int decode_rows_per_wg(int M, int h_kv, int kind) {
-  if (decode_r128_shape(M, h_kv, kind)) return 128;
+  (void)kind;
   return 16 * decode_row_blocks_per_wg(h_kv > 1 ? M / h_kv : M);
 }
 
 // Name of the instantiation launch_decode runs for this shape (as profilers
 // print it, without namespaces and parameter list).
 const char* decode_kernel_name(int M, int h_kv, int kind) {
-  if (decode_r128_shape(M, h_kv, kind)) return kind == kDecodeF16 ? "decode_r128_kernel<true>" : "decode_r128_kernel<false>";
   if (kind == kDecodeFp8Packed) return "decode_fp8ws_kernel<false>";
   if (kind == kDecodeFp8Indexed) return "decode_fp8ws_kernel<true>";
   static const char* const names[3][2][2] = {
@@ -1580,7 +1579,6 @@ const char* decode_kernel_name(int M, int h_kv, int kind) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int kind, hipStream_t stream) {
-  if (decode_r128_shape(a.M, a.h_kv, kind)) return launch_decode_r128(a, kind, stream);
   switch (decode_row_blocks_per_wg(a.h_kv > 1 ? a.Mkv : a.M)) {
     case 1: return launch_decode_t<1>(a, kind, stream);
     case 2: return launch_decode_t<2>(a, kind, stream);
@@ -1603,11 +1601,6 @@ static hipError_t occupancy_t(int kind, int* n) {
 hipError_t decode_occupancy(int kind, int M, int* wgs_per_cu) {
   int n = 0;
   hipError_t e;
-  if (decode_r128_shape(M, 1, kind)) {
-    e = decode_r128_occupancy(kind, &n);
-    *wgs_per_cu = n;
-    return e;
-  }
   switch (decode_row_blocks_per_wg(M)) {
     case 1: e = occupancy_t<1>(kind, &n); break;
     case 2: e = occupancy_t<2>(kind, &n); break;
@@ -1867,10 +1860,8 @@ hipError_t read_and_clear_error_flags(int* flags, hipStream_t stream) {
   int zero = 0;
   e = hipMemcpyToSymbol(HIP_SYMBOL(g_error_flags), &zero, sizeof(int), 0, hipMemcpyHostToDevice);
   if (e != hipSuccess) return e;
-  int v2 = 0;
-  e = read_and_clear_error_flags_r128(&v2);
-  *flags = v | v2;
-  return e;
+  *flags = v;
+  return hipSuccess;
 }
 
 }  // namespace mla

@@ -14,12 +14,6 @@ LSE_ATOL = 1e-3
 REL_RMS_ALARM = 1e-2
 
 
-def uses_r128_kernel(rows_per_request, h_kv=1, fp8=False):
-    """Whether the library runs the 128-row dense kernel for this shape (one KV
-    head, 256 or more rows per request, a multiple of 128)."""
-    return not fp8 and h_kv == 1 and rows_per_request >= 256 and rows_per_request % 128 == 0
-
-
 def say(msg):
     print(msg, flush=True)
     sys.stdout.flush()

@@ -56,8 +56,8 @@ def test_decode_workspace_size_formula():
     (64, 1, 128, 256, 1, 128),      # 64-row kernel: two row blocks per request -> 256 WG slots / 2
     (1, 1, 128, 256, 1, 16),        # capped at 16 pieces per request
     (8, 1, 64, 256, 1, 128),        # 64-row kernel, one row block: 8 requests x 16
-    (16, 2, 128, 256, 1, 128),      # 256 rows: 128-row kernel, two row blocks per request
-    (4, 4, 128, 256, 1, 64),        # 512 rows: four 128-row blocks, 4 x 16
+    (16, 2, 128, 256, 1, 64),       # 256 rows: four row blocks per request -> 256 / 4
+    (4, 4, 128, 256, 1, 32),        # 512 rows: eight row blocks, 256 / 8
     (4, 1, 96, 256, 1, 64),         # 96 rows: two 64-row blocks (64-row kernel), 4 x 16
     (1, 1, 16, 256, 1, 16),
     (1000, 1, 128, 256, 1, 128),
@@ -89,8 +89,8 @@ def test_plan_num_parts_multi_kv_head(batch, s_q, h_q, h_kv):
     (1, 128, 1, ops.KV_BF16_PAGED, "decode_ws_kernel<4, false, false>"),   # 128 rows: two 64-row workgroups
     (1, 16, 1, ops.KV_BF16_PAGED, "decode_ws_kernel<1, false, false>"),
     (1, 32, 1, ops.KV_FP16_PAGED, "decode_ws_kernel<2, true, false>"),
-    (2, 128, 1, ops.KV_BF16_PAGED, "decode_r128_kernel<false>"),          # 256 rows: the 128-row kernel
-    (4, 128, 1, ops.KV_FP16_PAGED, "decode_r128_kernel<true>"),
+    (2, 128, 1, ops.KV_BF16_PAGED, "decode_ws_kernel<4, false, false>"),  # 256 rows: four 64-row workgroups
+    (4, 128, 1, ops.KV_FP16_PAGED, "decode_ws_kernel<4, true, false>"),
     (2, 128, 2, ops.KV_BF16_PAGED, "decode_ws_kernel<4, false, true>"),    # several KV heads
     (1, 64, 1, ops.KV_FP8_PACKED, "decode_fp8ws_kernel<false>"),
     (16, 128, 1, ops.KV_FP8_INDEXED, "decode_fp8ws_kernel<true>"),
