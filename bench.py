@@ -63,7 +63,7 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 FLUSH_BYTES = 512 << 20
 ROUNDS = 5
-PROFILE_PMC = os.path.join(ROOT, "profiles", "decode_kernel_h_pmc.md")
+PROFILE_PMC = os.path.join(ROOT, "profiles", "decode_kernel_h_profile.md")
 KERNEL_SRCS = sorted(glob.glob(os.path.join(ROOT, "mla_paged_kv_amd", "csrc", "*.hip"))) + [
     os.path.join(ROOT, "mla_paged_kv_amd", "csrc", "mla_internal.h")]
 
