@@ -228,6 +228,20 @@ def test_long_context_sk65536(parts):
     assert ops.mla_read_device_errors() == 0
 
 
+def test_batch_128_ragged_every_row():
+    """b=128 (the top of the dense page's test range) with ragged lengths from 1 to
+    2048 tokens, at the library's split count, every row against the oracle."""
+    G.say("b=128 ragged")
+    rng = np.random.default_rng(197)
+    seqlens = rng.integers(1, 2048, size=128, endpoint=True).astype(np.int32)
+    pages = int(sum((int(n) + 63) // 64 for n in seqlens))
+    w = W.dense_workload("b128", 197, 128, 1, 128, seqlens, pool_pages=pages + 16)
+    out, lse, plan = G.run_dense(w)
+    G.say(f"  num_parts={plan.num_parts}")
+    G.compare("b128-ragged", out, lse, *oracle_dense(w))
+    assert ops.mla_read_device_errors() == 0
+
+
 @pytest.mark.parametrize("parts", [128, 200])
 def test_combine_more_than_64_splits(parts):
     """One request cut into more than 64 splits: the combine's lse reductions
@@ -452,6 +466,8 @@ SPARSE_MULTI = [
     ("sq4-h64-tails", 159, 3, 64, 128, [128, 70, 1], 1024, 4, None),
     ("sq8-h64-p3", 160, 2, 64, 192, [150, 192], 4096, 8, 3),
     ("sq16-h128", 161, 2, 128, 128, [128, 90], 1024, 16, None),
+    ("sq3-h64-tails", 162, 3, 64, 256, [256, 130, 3], 2048, 3, None),   # three tokens: the packed page's S_q = 3
+    ("sq3-h128-p5", 163, 2, 128, 192, [192, 61], 2048, 3, 5),
 ]
 
 
