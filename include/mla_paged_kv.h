@@ -35,6 +35,10 @@
  *     [0, num_pages * 64).  The kernels bounds-check them anyway, never read
  *     out of range, and record a violation in a device flag that
  *     mla_read_device_errors() returns.
+ *   - With MLA_LOG set (and not "0") in the environment, every launch prints
+ *     one line to stderr: for the decode its kernel instantiation, grid, block,
+ *     split count, resident workgroups per CU, static LDS bytes and VGPRs; for
+ *     the other kernels their main sizes.
  *
  * Layouts (all row-major, contiguous):
  *   q            bf16  [batch][s_q][h_q][576]

@@ -8,6 +8,7 @@
 #include "../../include/mla_paged_kv.h"
 
 #include <stdarg.h>
+#include <stdlib.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -33,6 +34,16 @@ int fail(int code, const char* fmt, ...) {
 int ok() {
   g_last_error.clear();
   return MLA_OK;
+}
+
+// MLA_LOG=1 in the environment: one line per launch on stderr (decode: kernel,
+// grid, split count, resident workgroups per CU, LDS bytes, VGPRs).
+bool log_on() {
+  static const bool on = [] {
+    const char* v = getenv("MLA_LOG");
+    return v && *v && strcmp(v, "0") != 0;
+  }();
+  return on;
 }
 
 int hip_fail(hipError_t e, const char* what) {
@@ -164,6 +175,15 @@ int launch_decode_checked(const void* q, const void* kv, int kv_format, int64_t 
                                                      : mla::kDecodeBf16;
   hipError_t e = mla::launch_decode(a, kind, stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
+  if (log_on()) {
+    mla::DecodeLaunchInfo info;
+    if (mla::decode_launch_info(a, kind, &info) == hipSuccess)
+      fprintf(stderr,
+              "[mla] decode %s grid=%dx%d block=%d num_parts=%d wgs_per_cu=%d lds=%d vgprs=%d batch=%d s_q=%d "
+              "h_q=%d h_kv=%d\n",
+              info.name, info.grid_x, info.grid_y, info.block, num_parts, info.wgs_per_cu, info.lds_bytes, info.vgprs,
+              batch, s_q, h_q, h_kv);
+  }
   return ok();
 }
 
@@ -176,6 +196,9 @@ int launch_combine_checked(const int32_t* num_splits, const void* workspace, int
   hipError_t e = mla::launch_combine(num_splits, part_o, part_lse, batch, M, slots_for(batch, num_parts),
                                      kv_format == MLA_KV_FP16_PAGED, (uint16_t*)out, lse, stream);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
+  if (log_on())
+    fprintf(stderr, "[mla] combine batch=%d rows=%d slots=%d num_parts=%d\n", batch, M, slots_for(batch, num_parts),
+            num_parts);
   return ok();
 }
 
@@ -257,6 +280,7 @@ int mla_get_decode_metadata(const int32_t* seqlens, int batch, int s_q, int h_q,
   if (st) return st;
   hipError_t e = mla::launch_sched(seqlens, batch, num_parts, sched_meta, num_splits, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "scheduler launch");
+  if (log_on()) fprintf(stderr, "[mla] metadata global batch=%d num_parts=%d\n", batch, num_parts);
   return ok();
 }
 
@@ -283,6 +307,8 @@ int mla_get_packed_decode_metadata(const int32_t* topk_length, int batch, int s_
   const bool local = policy == MLA_SCHED_REQUEST_LOCAL;
   hipError_t e = mla::launch_sched(topk_length, batch, num_parts, sched_meta, num_splits, (hipStream_t)stream, local);
   if (e != hipSuccess) return hip_fail(e, "scheduler launch");
+  if (log_on())
+    fprintf(stderr, "[mla] metadata %s batch=%d num_parts=%d\n", local ? "request-local" : "global", batch, num_parts);
   return ok();
 }
 
@@ -362,6 +388,7 @@ int mla_pack_selected_kv(const void* kcache_fp8, int64_t num_pages, const int32_
   hipError_t e = mla::launch_pack((const uint8_t*)kcache_fp8, num_pages, indices, topk_length, batch, s_q,
                                   topk_capacity, (uint8_t*)workspace, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "pack launch");
+  if (log_on()) fprintf(stderr, "[mla] pack rows=%d topk_capacity=%d\n", batch * s_q, topk_capacity);
   return ok();
 }
 
@@ -387,6 +414,7 @@ int mla_patch_packed_kv(const void* kcache_fp8, int64_t num_pages, const int32_t
   hipError_t e = mla::launch_patch((const uint8_t*)kcache_fp8, num_pages, indices, topk_length, new_ids, n_new, batch,
                                    s_q, topk_capacity, (uint8_t*)workspace, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "patch launch");
+  if (log_on()) fprintf(stderr, "[mla] patch rows=%d topk_capacity=%d n_new=%d\n", batch * s_q, topk_capacity, n_new);
   return ok();
 }
 

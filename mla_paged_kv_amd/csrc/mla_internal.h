@@ -51,6 +51,13 @@ int decode_row_blocks_per_wg(int M);
 int decode_rows_per_wg(int M, int h_kv, int kind);
 const char* decode_kernel_name(int M, int h_kv, int kind);
 
+// What launch_decode would launch for these arguments (for MLA_LOG).
+struct DecodeLaunchInfo {
+  const char* name;
+  int grid_x, grid_y, block, lds_bytes, vgprs, wgs_per_cu;
+};
+hipError_t decode_launch_info(const struct DecodeArgs& a, int kind, DecodeLaunchInfo* info);
+
 hipError_t launch_sched(const int32_t* lengths, int batch, int num_parts, int32_t* meta, int32_t* num_splits,
                         hipStream_t stream, bool request_local = false);
 // Decode kernel family: bf16 pages, FP8 packed workspace, FP8 pool gathered by

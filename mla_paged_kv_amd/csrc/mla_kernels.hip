@@ -1598,6 +1598,34 @@ static hipError_t occupancy_t(int kind, int* n) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, decode_ws_kernel<RB, false, false>, kWsThreads, 0);
 }
 
+template <int RB>
+static const void* decode_fn_t(int kind, bool mkv) {
+  if (kind == kDecodeFp8Packed) return reinterpret_cast<const void*>(decode_fp8ws_kernel<false>);
+  if (kind == kDecodeFp8Indexed) return reinterpret_cast<const void*>(decode_fp8ws_kernel<true>);
+  if (kind == kDecodeF16)
+    return mkv ? reinterpret_cast<const void*>(decode_ws_kernel<RB, true, true>)
+               : reinterpret_cast<const void*>(decode_ws_kernel<RB, true, false>);
+  return mkv ? reinterpret_cast<const void*>(decode_ws_kernel<RB, false, true>)
+             : reinterpret_cast<const void*>(decode_ws_kernel<RB, false, false>);
+}
+
+hipError_t decode_launch_info(const DecodeArgs& a, int kind, DecodeLaunchInfo* info) {
+  const int rb = decode_row_blocks_per_wg(a.h_kv > 1 ? a.Mkv : a.M);
+  const int MB = 16 * rb;
+  const void* fn = rb == 1 ? decode_fn_t<1>(kind, a.h_kv > 1) : rb == 2 ? decode_fn_t<2>(kind, a.h_kv > 1)
+                                                                        : decode_fn_t<4>(kind, a.h_kv > 1);
+  info->name = decode_kernel_name(a.M, a.h_kv, kind);
+  info->grid_x = a.num_parts;
+  info->grid_y = a.h_kv > 1 ? a.h_kv * ((a.Mkv + MB - 1) / MB) : (a.M + MB - 1) / MB;
+  info->block = kWsThreads;
+  hipFuncAttributes attr;
+  hipError_t e = hipFuncGetAttributes(&attr, fn);
+  if (e != hipSuccess) return e;
+  info->lds_bytes = (int)attr.sharedSizeBytes;
+  info->vgprs = attr.numRegs;
+  return decode_occupancy(kind, a.h_kv > 1 ? a.Mkv : a.M, &info->wgs_per_cu);
+}
+
 hipError_t decode_occupancy(int kind, int M, int* wgs_per_cu) {
   int n = 0;
   hipError_t e;

@@ -746,3 +746,92 @@ def test_hip_graph_replay_matches_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"replay {rep} differs from the eager step"
+
+
+# ----------------------------------------------------------------------------- launch log, canaries
+
+def test_mla_log_prints_launch_lines():
+    """MLA_LOG=1: one stderr line per launch, the decode's with its kernel, grid,
+    split count, occupancy, LDS and VGPRs (checked in a child process, since the
+    library reads the variable once)."""
+    import os
+    import subprocess
+    import sys
+
+    code = ("import numpy as np, torch\n"
+            "from mla_paged_kv_amd import ops, workloads as W\n"
+            "from tests import gpu_helpers as G\n"
+            "w = W.dense_workload('log', 301, 2, 1, 128, [300, 70], pool_pages=8)\n"
+            "G.run_dense(w)\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, MLA_LOG="1", PYTHONPATH=root)
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, env=env, capture_output=True, text=True, timeout=120)
+    G.say(r.stderr[-600:])
+    assert r.returncode == 0
+    lines = [ln for ln in r.stderr.splitlines() if ln.startswith("[mla]")]
+    dec = [ln for ln in lines if ln.startswith("[mla] decode")]
+    assert len(dec) == 1 and "decode_ws_kernel<4, false, false>" in dec[0]
+    for key in ("grid=", "num_parts=", "wgs_per_cu=", "lds=", "vgprs="):
+        assert key in dec[0]
+    assert any(ln.startswith("[mla] metadata") for ln in lines)
+    assert any(ln.startswith("[mla] combine") for ln in lines)
+
+
+def _padded(numel, dtype, canary):
+    """A device buffer of `numel` elements with 4096 canary elements on each side;
+    returns (whole buffer, the middle view)."""
+    pad = 4096
+    whole = torch.full((numel + 2 * pad,), canary, dtype=dtype, device="cuda")
+    return whole, whole[pad:pad + numel]
+
+
+def _canaries_intact(whole, canary):
+    pad = 4096
+    return bool(torch.all(whole[:pad] == canary)) and bool(torch.all(whole[-pad:] == canary))
+
+
+@pytest.mark.parametrize("fmt", ["dense", "packed", "indexed"])
+def test_no_writes_outside_the_buffers(fmt):
+    """Canary-padded out, lse, workspace, metadata and packed workspace: no kernel
+    writes outside the memory it was given."""
+    G.say(f"canaries {fmt}")
+    if fmt == "dense":
+        w = W.dense_workload("canary", 302, 3, 2, 128, [1, 700, 129], pool_pages=20, causal=True, num_parts=5)
+    else:
+        w = W.sparse_workload("canary", 303, 3, 64, 256, [256, 70, 1], context=1024, s_q=2, num_parts=5)
+    t = G.dev_tensors(w)
+    b, s_q, h_q = w.batch, w.s_q, w.h_q
+    P = w.num_parts
+    ow, out_flat = _padded(b * s_q * h_q * 512, torch.int16, 0x7a5b)
+    lw, lse_flat = _padded(b * s_q * h_q, torch.float32, -12345.5)
+    mw, meta_flat = _padded(P * 8, torch.int32, 0x5a5a5a5a)
+    nw, ns = _padded(b + 1, torch.int32, 0x5a5a5a5a)
+    ww, ws = _padded(ops.mla_decode_workspace_size(b, s_q, h_q, P), torch.uint8, 0xA5)
+    act = torch.bfloat16
+    out = out_flat.view(act).view(b, s_q, h_q, 512)
+    lse = lse_flat.view(b, s_q, h_q)
+    meta = meta_flat.view(P, 8)
+    if fmt == "dense":
+        fmt_id, kv, ix = ops.KV_BF16_PAGED, t["kcache"], t["block_table"]
+        ops.mla_get_decode_metadata(t["seqlens"], b, s_q, h_q, 1, P, meta, ns)
+        cap = 0
+    else:
+        cap = w.topk_capacity
+        ops.mla_get_decode_metadata(t["seqlens"], b, s_q, h_q, 1, P, meta, ns)
+        if fmt == "packed":
+            pw, pws = _padded(ops.mla_packed_kv_workspace_size(b, s_q, cap), torch.uint8, 0xA5)
+            ops.mla_pack_selected_kv(t["kcache_rec"], t["indices"], t["seqlens"], pws)
+            torch.cuda.synchronize()
+            assert _canaries_intact(pw, 0xA5)
+            fmt_id, kv, ix = ops.KV_FP8_PACKED, pws, None
+        else:
+            fmt_id, kv, ix = ops.KV_FP8_INDEXED, t["kcache_rec"], t["indices"]
+    ops.mla_decode_fwd(t["q"], kv, fmt_id, ix, t["seqlens"], w.scale, w.causal, meta, ns, out, lse, ws,
+                       topk_capacity=cap)
+    ops.mla_combine(ns, ws, b, s_q, h_q, P, out, lse)
+    torch.cuda.synchronize()
+    for whole, canary in ((ow, 0x7a5b), (lw, -12345.5), (mw, 0x5a5a5a5a), (nw, 0x5a5a5a5a), (ww, 0xA5)):
+        assert _canaries_intact(whole, canary)
+    ref = oracle_dense(w) if fmt == "dense" else oracle_sparse(w)
+    G.compare(f"canary-{fmt}", out, lse, *ref)
+    assert ops.mla_read_device_errors() == 0
