@@ -17,18 +17,22 @@ the 256 MB Infinity Cache).
                    bound).
   decode_combine   the same loop without the metadata kernel (the metadata is
                    computed once per step and reused by every layer).
-  kernels_ms       per-kernel HIP-event durations from a separate loop with an
-                   event between kernels.
+  kernels_ms       the decode alone launched K times back to back between two
+                   HIP events (its mean duration), and per-kernel HIP-event
+                   durations from a loop with an event between the kernels.
   graph_ms_per_step  the step replayed as a HIP graph (checked bitwise against
                    the eager step first).
   roofline         the decode kernel: algorithmic KV bytes per launch / its mean
-                   event duration, against 8 TB/s; `traffic` is the HBM bytes per
+                   duration back to back (HIP events), against 8 TB/s; `traffic` is the HBM bytes per
                    launch from the committed counter summary when it was taken on
                    the current kernel sources, else null.
   copy_bandwidth   a measured 1 GiB device-to-device copy (read + write bytes /
                    time), and value as a share of it.
-  cpu_baseline     the fp64 oracle on the whole workload on the host cores (after
-                   the GPU output of the same run was checked against it).
+  cpu_baseline     the fp64 oracle on the whole workload on the host cores, run
+                   after the GPU measurements; the first step's output is checked
+                   against it before anything is printed.
+Before the W warmup steps, untimed steps run back to back for --warm-seconds so
+that the GPU clock has ramped up when the measurements start.
 
 Other modes (one JSON line per case):
   --configs   the five seeded test configurations and the headline shape, each
@@ -311,6 +315,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--num-parts", type=int, default=0, help="force the split count (0 = library choice)")
+    ap.add_argument("--warm-seconds", type=float, default=0.5,
+                    help="untimed back-to-back steps before the warmup steps (the GPU clock ramps up)")
     ap.add_argument("--oracle-requests", type=int, default=64, help="requests in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg (profiling runs)")
     ap.add_argument("--no-graph", action="store_true",
@@ -359,25 +365,22 @@ def main():
     kv_bytes, flops = w.kv_bytes(), w.flops()
     stream = torch.cuda.current_stream()
 
-    # ---- parity gate + CPU baseline (the oracle on the same workload)
+    # ---- the first step's output is kept for the parity gate, which runs after
+    # the GPU measurements (the oracle keeps the host busy for seconds, and an
+    # idle GPU drops its clock)
     case.step(0)
     torch.cuda.synchronize()
-    cpu_baseline = None
-    if not args.no_cpu_baseline:
-        from oracle import oracle as orc
+    out0, lse0 = case.out.clone(), case.lse.clone()
 
-        threads = orc.default_threads()
-        sel = list(np.linspace(0, b - 1, args.oracle_requests).astype(int))
-        dt, sub = cpu_leg_dense(w, case.out, case.lse, sel, threads)
-        cpu_baseline = {
-            "value": round(sub.kv_bytes() / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(sel)} of {b} requests (all {h_q} heads, {int(w.seqlens[0])} keys each), fp64, "
-                      f"{sub.flops() / dt / 1e9:.2f} GFLOP/s, {dt:.2f} s wall",
-            **cpu_info(),
-        }
-        log(f"oracle: {dt:.2f}s on {threads} threads; parity ok")
-
-    # ---- warmup, then per-kernel event times
+    # ---- untimed: back-to-back steps for --warm-seconds (the clock ramps up),
+    # then the W warmup steps, then per-kernel event times
+    t_warm = time.perf_counter()
+    n_warm = 0
+    while time.perf_counter() - t_warm < args.warm_seconds:
+        for i in range(10):
+            case.step(n_warm + i)
+        n_warm += 10
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         case.step(i)
     kt = kernel_event_times(torch, stream, args.steps,
@@ -388,6 +391,9 @@ def main():
     reg = timed_region(torch, stream, args.steps, case.step)
     case.c_meta()
     reg_dc = timed_region(torch, stream, args.steps, lambda i: (case.c_dec[i % 2](), case.c_comb()))
+    # the decode kernel alone: K launches back to back between two events (its
+    # mean launch duration, without the gaps an event between kernels adds)
+    reg_dec = timed_region(torch, stream, args.steps, lambda i: case.c_dec[i % 2]())
     ms_per_step = reg["wall_ms_per_step"]
 
     # ---- the step as a HIP graph (one per pool copy), checked bitwise against
@@ -424,8 +430,25 @@ def main():
     if flags:
         raise SystemExit(f"device error flags set: {flags}")
 
+    # ---- parity gate + CPU baseline (the oracle on the same workload): raises
+    # before anything is printed if the first step's output disagrees
+    cpu_baseline = None
+    if not args.no_cpu_baseline:
+        from oracle import oracle as orc
+
+        threads = orc.default_threads()
+        sel = list(np.linspace(0, b - 1, args.oracle_requests).astype(int))
+        dt, sub = cpu_leg_dense(w, out0, lse0, sel, threads)
+        cpu_baseline = {
+            "value": round(sub.kv_bytes() / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(sel)} of {b} requests (all {h_q} heads, {int(w.seqlens[0])} keys each), fp64, "
+                      f"{sub.flops() / dt / 1e9:.2f} GFLOP/s, {dt:.2f} s wall",
+            **cpu_info(),
+        }
+        log(f"oracle: {dt:.2f}s on {threads} threads; parity ok")
+
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    dec_mean_s = float(dec_ms.mean()) * 1e-3
+    dec_mean_s = reg_dec["event_span_ms_per_step"] * 1e-3
     achieved = kv_bytes / dec_mean_s / 1e9
     dc_ms = reg_dc["wall_ms_per_step"]
     emit({
@@ -448,6 +471,7 @@ def main():
             "num_parts": case.num_parts, "kv_bytes_per_step": kv_bytes, "flops_per_step": flops,
             "cold_kv": "two pool copies alternate per step",
             "launch": "pre-bound C-ABI calls on one stream (metadata, decode, combine)",
+            "untimed_warm": f"{n_warm} steps over {args.warm_seconds} s, then the {args.warmup} warmup steps",
         },
         "timed_region": reg,
         "decode_combine": {**reg_dc, "GBps": round(kv_bytes / (dc_ms * 1e-3) / 1e9, 2),
@@ -458,11 +482,14 @@ def main():
         "copy_bandwidth": {"measured_GBps": copy_gbs, "pct_of_measured_copy": round(100.0 * value / copy_gbs, 2),
                            "method": "1 GiB device-to-device copy, (read + write bytes) / median of 10"},
         "kernels_ms": {
+            "decode_back_to_back": round(reg_dec["event_span_ms_per_step"], 5),
             "metadata": round(float(meta_ms.mean()), 5),
             "decode": round(float(dec_ms.mean()), 5),
             "decode_median": round(float(np.median(dec_ms)), 5),
             "decode_min": round(float(dec_ms.min()), 5),
             "combine": round(float(comb_ms.mean()), 5),
+            "note": "decode_back_to_back: event span of K decode launches / K (roofline.achieved uses it); "
+                    "the others: events between the kernels of each step",
         },
         "roofline": {
             "bound": "hbm",
@@ -530,6 +557,12 @@ def profile_loop(args):
                       ops.mla_combine(p.num_splits, p.workspace, b, s_q, h_q, p.num_parts, out, lse, bind=True)]
         step = lambda i: [c() for c in calls]  # noqa: E731
         log(f"profile loop {args.workload}: pack, packed and by-index decode")
+    t_warm = time.perf_counter()
+    n_warm = 0
+    while time.perf_counter() - t_warm < args.warm_seconds:
+        step(n_warm)
+        n_warm += 1
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
     reg = timed_region(torch, stream, args.steps, step)
