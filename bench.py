@@ -174,6 +174,18 @@ def kernel_event_times(torch, stream, steps, calls_of_step):
     return np.array([[e[k].elapsed_time(e[k + 1]) for k in range(n)] for e in evs])
 
 
+def gpu_warm(torch, step, seconds):
+    """Untimed back-to-back calls of step(i) for `seconds` (the clock ramps up)."""
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for i in range(10):
+            step(n + i)
+        n += 10
+        torch.cuda.synchronize()
+    return n
+
+
 class Flusher:
     """Reads a buffer larger than the 256 MB Infinity Cache (and every L2), so
     that what follows reads its inputs from HBM.  A read, not a write: a
@@ -374,13 +386,7 @@ def main():
 
     # ---- untimed: back-to-back steps for --warm-seconds (the clock ramps up),
     # then the W warmup steps, then per-kernel event times
-    t_warm = time.perf_counter()
-    n_warm = 0
-    while time.perf_counter() - t_warm < args.warm_seconds:
-        for i in range(10):
-            case.step(n_warm + i)
-        n_warm += 10
-        torch.cuda.synchronize()
+    n_warm = gpu_warm(torch, case.step, args.warm_seconds)
     for i in range(args.warmup):
         case.step(i)
     kt = kernel_event_times(torch, stream, args.steps,
@@ -641,6 +647,7 @@ def configs_main(args):
     for n in names:
         cases[n] = DenseCase(torch, ops, W.config(n), dev)
         log(f"{n}: {cases[n].kernel}, {cases[n].num_parts} parts")
+    gpu_warm(torch, cases["h"].step, args.warm_seconds)
     copy_gbs = copy_bandwidth(torch, dev)
     rounds = _dense_cold_rounds(torch, cases, args.reps, flush, stream)
     # hot too: repetitions back to back, inputs left in the caches by the previous one
@@ -778,6 +785,7 @@ def sweep_main(args):
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     flush = Flusher(torch, dev)
+    gpu_warm(torch, lambda i: flush(), args.warm_seconds)
     copy_gbs = copy_bandwidth(torch, dev)
     log(f"measured copy bandwidth {copy_gbs} GB/s")
     if args.sweep_part in ("dense", "both"):
@@ -795,6 +803,7 @@ def sweep_main(args):
 
                 cpu_leg_dense(w, cases[name].out, cases[name].lse, [0], orc.default_threads())
             log(f"{name}: {cases[name].kernel}, {cases[name].num_parts} parts")
+        gpu_warm(torch, next(iter(cases.values())).step, args.warm_seconds)
         rounds = _dense_cold_rounds(torch, cases, args.reps, flush, stream)
         for name, c in cases.items():
             dc_med = float(np.median(rounds[name][:, 1] + rounds[name][:, 2]))
@@ -804,6 +813,7 @@ def sweep_main(args):
         del cases
         torch.cuda.empty_cache()
     if args.sweep_part in ("packed", "both"):
+        gpu_warm(torch, lambda i: flush(), args.warm_seconds)
         k = 0
         for h in PACKED_GRID_H:
             for b in PACKED_GRID_B:
