@@ -107,11 +107,12 @@ const char* mla_last_error_message(void);
 /* Recommended split count (partitions of the KV work) for a decode launch on
  * the current device: workgroups that fit per CU (from the compiled kernel's
  * LDS and register footprint, via the HIP occupancy query) times the CU
- * count, divided by the row blocks per request, then capped so that no
- * request is cut into more pieces than an empirical limit (the partition count
- * is scaled to resident workgroups rather than to the CU count, and gated by
- * measured limits: "How the occupancy work went", FlashMLA PR 183).  Host
- * only; queries the device. */
+ * count, divided by the row blocks per request, then capped at an empirical
+ * number of pieces per request: 64 for the 16-bit formats (of which
+ * mla_get_decode_metadata uses only what the lengths call for) and 32 for the
+ * FP8 formats (the partition count is scaled to resident workgroups rather
+ * than to the CU count, and gated by measured limits: "How the occupancy work
+ * went", FlashMLA PR 183).  Host only; queries the device. */
 int mla_decode_num_parts(int batch, int s_q, int h_q, int h_kv, int kv_format, int* num_parts_out);
 
 /* The same policy as a pure function of the device figures (for tests and for
@@ -145,10 +146,13 @@ size_t mla_packed_kv_workspace_size(int batch, int s_q, int topk_capacity);
  * blocks of all requests into num_parts contiguous partitions.  Definition:
  * request r has
  * ceil(seqlens[r] / 64) blocks (seqlens = topk_length for the packed path),
- * T blocks in total, and P' = min(num_parts, T); concatenating all requests'
- * blocks in order, partition p < P' owns global blocks
- * [floor(p*T/P'), floor((p+1)*T/P')) -- at least one -- and partitions
- * p >= P' own none.
+ * T blocks in total, and P' = min(num_parts, T, L) partitions are used, with
+ * the split limit L = max(16 * batch, min(ceil(T / 4), 64 * batch)) (enough
+ * pieces to spread long requests over the GPU, not so many that short ones
+ * pay for partials they do not need; measured, see mla_decode_num_parts);
+ * concatenating all requests' blocks in order, partition p < P' owns global
+ * blocks [floor(p*T/P'), floor((p+1)*T/P')) -- at least one -- and
+ * partitions p >= P' own none.
  *   sched_meta[p] = { begin_req, begin_block, end_req, end_block_exclusive,
  *                     split index of the first piece within begin_req, 0, 0, 0 }
  *                   or { -1, -1, -1, -1, -1, 0, 0, 0 } for an empty partition;
@@ -170,7 +174,8 @@ typedef enum {
  * get_packed_mla_metadata call of "[SM90] Add packed selected-KV sparse
  * decode" (FlashMLA PR 200, Python API, Scheduler policy).  Same outputs and
  * format as mla_get_decode_metadata, over topk_length.
- *   MLA_SCHED_GLOBAL: exactly mla_get_decode_metadata's partition.
+ *   MLA_SCHED_GLOBAL: mla_get_decode_metadata's partition without the
+ *     split limit (P' = min(num_parts, T)).
  *   MLA_SCHED_REQUEST_LOCAL: the page's "compact request-local scheduler",
  *     which it names without defining; here: with b_r = ceil(topk_length[r] /
  *     64) blocks, B = the smallest piece size with sum_r ceil(b_r / B) <=

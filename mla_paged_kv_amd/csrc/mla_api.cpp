@@ -50,15 +50,19 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Empirical partition gate: at most this many pieces per request.  Each extra
-// piece re-reads the request's Q rows, runs a prologue/epilogue and writes a
-// 128 x 513 fp32 partial that the combine re-reads, so splitting finer than
-// the occupancy needs costs bandwidth.  Measured on MI355X (HIP-graph step,
-// metadata + decode + combine): for the bf16 kernel 16 and 32 pieces per
-// request are within +-4 % at b = 1..16, sk = 1024..8192, and 64 is slower at
-// b = 1; the FP8 kernel is slower per tile and gains from finer pieces (C5:
-// 45.9 us at 16 per request, 38.7 us at 32, 38.5 us at 64).
-constexpr int kMaxSplitsPerRequest = 16;
+// Empirical partition gates.  Each extra piece re-reads the request's Q rows,
+// runs a prologue/epilogue and writes a 128 x 513 fp32 partial that the
+// combine re-reads, so splitting finer than the work needs costs bandwidth,
+// while too few pieces leave CUs idle on long requests.  The 16-bit paths: the
+// plan allows up to 64 pieces per request and the device scheduler, which
+// sees the lengths, uses at most max(16 b, min(ceil(T / 4), 64 b)) of them
+// (mla_internal.h).  Measured on MI355X (decode + combine, cold KV, h_q 128):
+// b = 1 takes 21.7 / 27.6 / 36.6 / 60.5 us at sk = 1024 / 4096 / 16384 / 65536
+// with 16 / 16 / 64 / 64 pieces, against 47.8 and 129.0 us for the last two at
+// 16; b = 4, sk = 4096 is fastest at 64 (32.0 us against 33.5 at 128).  The
+// FP8 kernel is slower per tile and gains from finer pieces (C5: 45.9 us at 16
+// per request, 38.7 us at 32, 38.5 us at 64).
+constexpr int kMaxSplitsPerRequest = mla::kSplitCeilPerRequest;
 constexpr int kMaxSplitsPerRequestFp8 = 32;
 
 bool is_gfx950() {
@@ -278,7 +282,8 @@ int mla_get_decode_metadata(const int32_t* seqlens, int batch, int s_q, int h_q,
   if (st) return st;
   st = check_device();
   if (st) return st;
-  hipError_t e = mla::launch_sched(seqlens, batch, num_parts, sched_meta, num_splits, (hipStream_t)stream);
+  hipError_t e =
+      mla::launch_sched(seqlens, batch, num_parts, sched_meta, num_splits, (hipStream_t)stream, false, true);
   if (e != hipSuccess) return hip_fail(e, "scheduler launch");
   if (log_on()) fprintf(stderr, "[mla] metadata global batch=%d num_parts=%d\n", batch, num_parts);
   return ok();

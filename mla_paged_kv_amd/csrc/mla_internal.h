@@ -58,8 +58,14 @@ struct DecodeLaunchInfo {
 };
 hipError_t decode_launch_info(const struct DecodeArgs& a, int kind, DecodeLaunchInfo* info);
 
+// Split limit of the dense scheduler: with T blocks over `batch` requests it
+// uses at most L = max(16 batch, min(ceil(T / 4), 64 batch)) partitions (see
+// mla_get_decode_metadata).
+constexpr int kSplitFloorPerRequest = 16;
+constexpr int kBlocksPerSplit = 4;
+constexpr int kSplitCeilPerRequest = 64;
 hipError_t launch_sched(const int32_t* lengths, int batch, int num_parts, int32_t* meta, int32_t* num_splits,
-                        hipStream_t stream, bool request_local = false);
+                        hipStream_t stream, bool request_local = false, bool split_limit = false);
 // Decode kernel family: bf16 pages, FP8 packed workspace, FP8 pool gathered by
 // index, fp16 pages.
 enum DecodeKind { kDecodeBf16 = 0, kDecodeFp8Packed = 1, kDecodeFp8Indexed = 2, kDecodeF16 = 3 };

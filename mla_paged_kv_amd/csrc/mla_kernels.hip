@@ -193,9 +193,10 @@ __device__ __forceinline__ uint32_t tile_off(int kr, int c) {
 
 // ------------------------------------------------------------------ scheduler
 // One workgroup.  Implements the partition definition in mla_paged_kv.h: request r
-// has ceil(len/64) blocks, T in all; with P' = min(P, T), part p < P' owns global
-// blocks [floor(pT/P'), floor((p+1)T/P')) and parts p >= P' own none, so the
-// parts owning one request's blocks are consecutive.
+// has ceil(len/64) blocks, T in all; with P' = min(P, T) (and, under the split
+// limit, min(P', L) with L = max(16 b, min(ceil(T/4), 64 b)) for b requests),
+// part p < P' owns global blocks [floor(pT/P'), floor((p+1)T/P')) and parts
+// p >= P' own none, so the parts owning one request's blocks are consecutive.
 constexpr int kSchedThreads = 256;
 
 __device__ __forceinline__ int64_t part_of_block(int64_t g, int64_t T, int64_t P);
@@ -330,7 +331,7 @@ __device__ bool request_local_partition(const int32_t* bl, int batch, int num_pa
 template <bool LOCAL>
 __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const int32_t* __restrict__ lengths, int batch,
                                                               int num_parts, int32_t* __restrict__ meta,
-                                                              int32_t* __restrict__ num_splits) {
+                                                              int32_t* __restrict__ num_splits, int split_limit) {
   __shared__ int32_t cum[kSchedMaxBatch + 1];
   __shared__ int32_t wsum[kSchedThreads / 64];
   const int t = threadIdx.x;
@@ -364,7 +365,12 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const int32_t* __r
   if (t == 0) cum[batch] = total;
   __syncthreads();
   const int64_t T = total;
-  const int64_t P = T < num_parts ? T : num_parts;  // P' (0 when there is no block at all)
+  int64_t P = T < num_parts ? T : num_parts;  // P' (0 when there is no block at all)
+  if (split_limit) {
+    const int64_t L = max((int64_t)kSplitFloorPerRequest * batch,
+                          min((T + kBlocksPerSplit - 1) / kBlocksPerSplit, (int64_t)kSplitCeilPerRequest * batch));
+    P = min(P, L);
+  }
 
   // 2. partition records
   for (int p = t; p < num_parts; p += kSchedThreads) {
@@ -653,15 +659,17 @@ __device__ __forceinline__ void qk_tile(const LDS_AS uint8_t* kt, uint32_t base0
 //     iteration t it computes S(t)^T = K(t) Q^T and, between those MFMAs, the
 //     online softmax of S(t-1) (kept in registers from the previous iteration),
 //     writing P(t-1) (bf16), the rescale factor and a flag to double-buffered
-//     LDS slots.  The VALU softmax thus runs in the shadow of the MFMAs.  They
-//     also stream the ring: tile t+2 goes into the slot of tile t-2 (whose K
-//     and V were read in iterations t-2 and t-1).  They finish their MFMAs
-//     before the PV waves do, so the issue stalls of the vector-memory path
-//     cost less on them (measured: 3-4 % faster than loads from the PV waves).
+//     LDS slots.  The VALU softmax thus runs in the shadow of the MFMAs.
 //   * PV waves 4..7: wave 4+w owns output columns [128w, 128w+128) for all rows
 //     (O in registers).  In iteration t it computes O += V(t-2)^T P(t-2)^T with
 //     V(t-2) held in registers and, after each 16-column block, reads the same
-//     block of V(t-1) from the ring into the freed registers.
+//     block of V(t-1) from the ring into the freed registers.  They also stream
+//     the ring: at the start of iteration t, tile t+2 goes into the slot of
+//     tile t-2 (whose K and V were read in iterations t-2 and t-1).  The QK
+//     waves carry the longer instruction stream per tile (softmax VALU next to
+//     LDS-fed MFMAs), so the ~36 vector-memory issues of a tile, which stall the
+//     issuing wave while the CU's address unit drains them, cost less on the PV
+//     waves (measured: decode 5-7 % faster than with the loads in the QK waves).
 // One barrier per 32-key tile ends iteration t: after it tile t+1 is resident,
 // P(t-1) is visible, and the V(t-1) reads of every PV wave have completed.  The
 // loop runs two extra iterations to drain the softmax and PV stages.
@@ -720,7 +728,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
   }
 
   TileLoader<false> loader;
-  loader.init(w, l);  // used by the QK waves (4 waves split a tile)
+  loader.init(w, l);  // used by the PV waves (4 waves split a tile)
   if constexpr (MKV) loader.init_rows(w, l);
   auto issue_tile = [&](int64_t page, int key0, int st) {
     if constexpr (MKV) loader.issue_page_hkv(a, page, key0, kvh, smem, st, w);
@@ -894,18 +902,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
         }
       };
 
-      // The QK waves also stream the ring: they finish their share of the MFMAs
-      // before the PV waves do, so the issue stalls of the vector-memory path
-      // cost less on them.  Tiles 0 and 1 now, tile t+2 at the start of
-      // iteration t.
-      if (ntile > 0) issue_tile(uniform(page_raw(0)), t0, 0);
-      if (ntile > 1) issue_tile(uniform(page_raw(1)), t0 + kTK, 1);
-      // page id of the tile the next iteration loads: read before the barrier that
-      // ends an iteration (which waits for it) and made wave-uniform after it
-      int pg_next = ntile > 2 ? page_raw(2) : 0;
-      if (ntile > 1) wait_vmcnt<kLPW>();
-      else wait_vmcnt<0>();
-      sync_lds();  // tile 0 resident
+      sync_lds();  // tile 0 resident (loaded by the PV waves)
       // one iteration; DO_QK: S(t) = QK^T(t), DO_SM: softmax of S(t-1) (in the
       // shadow of the MFMAs when both run); PAR = t & 1.  Instantiated per stage
       // combination and parity.
@@ -913,10 +910,6 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
         constexpr bool DO_QK = decltype(do_qk_c)::value;
         constexpr bool DO_SM = decltype(do_sm_c)::value;
         constexpr int PAR = decltype(par_c)::value;
-        // loads of tile t+2 into the slot of tile t-2 (its K was read in
-        // iteration t-2, its V in iteration t-1)
-        const bool more = t + 2 < ntile;
-        if (more) issue_tile(uniform(pg_next), t0 + (t + 2) * kTK, (t + 2) & 3);
         if (has_rows) {
           if constexpr (DO_QK) {
             const LDS_AS uint8_t* kt = smem + kOffKDense + (t & 3) * kTileBytes;
@@ -948,12 +941,6 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
             }
           }
         }
-        // own loads of tile t+1 done (tile t+2 may stay in flight)
-        if (t + 1 < ntile) {
-          if (more) wait_vmcnt<kLPW>();
-          else wait_vmcnt<0>();
-        }
-        if (t + 3 < ntile) pg_next = page_raw(t + 3);
         sync_lds();
       };
       using F = std::false_type;
@@ -1000,6 +987,14 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
                                          4, 5, 6, 7);
       };
 
+      // The ring: tiles 0 and 1 now, tile t+2 at the start of iteration t.
+      if (ntile > 0) issue_tile(uniform(page_raw(0)), t0, 0);
+      if (ntile > 1) issue_tile(uniform(page_raw(1)), t0 + kTK, 1);
+      // page id of the tile the next iteration loads: read before the barrier that
+      // ends an iteration (which waits for it) and made wave-uniform after it
+      int pg_next = ntile > 2 ? page_raw(2) : 0;
+      if (ntile > 1) wait_vmcnt<kLPW>();
+      else wait_vmcnt<0>();
       sync_lds();  // tile 0 resident
       // one iteration; DO_PV: PV(t-2) from registers, DO_VREAD: V(t-1) into
       // registers.  Instantiated per stage combination so that the steady-state
@@ -1012,6 +1007,10 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
           if (nvalid < kTK) zero_tail_rows_256(smem + kOffKDense + (t & 3) * kTileBytes, nvalid, 64 * w + l);
         }
         const int tp = t - 2, tv = t - 1;
+        // loads of tile t+2 into the slot of tile t-2 (its K was read in
+        // iteration t-2, its V in iteration t-1), before anything else
+        const bool more = t + 2 < ntile;
+        if (more) issue_tile(uniform(pg_next), t0 + (t + 2) * kTK, (t + 2) & 3);
         // PV(t-2) operands from LDS first: rescale flags and factors, P^T
         uint32_t fl = 0;
         float al[RB];
@@ -1047,6 +1046,12 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
 #pragma unroll
           for (int db = 0; db < 8; ++db) vread(tv, db);
         }
+        // own loads of tile t+1 done (tile t+2 may stay in flight)
+        if (t + 1 < ntile) {
+          if (more) wait_vmcnt<kLPW>();
+          else wait_vmcnt<0>();
+        }
+        if (t + 3 < ntile) pg_next = page_raw(t + 3);
         sync_lds();
       };
       using F = std::false_type;
@@ -1812,13 +1817,13 @@ __global__ __launch_bounds__(64) void patch_kernel(const uint8_t* __restrict__ k
 
 // ------------------------------------------------------------------ launchers
 hipError_t launch_sched(const int32_t* lengths, int batch, int num_parts, int32_t* meta, int32_t* num_splits,
-                        hipStream_t stream, bool request_local) {
+                        hipStream_t stream, bool request_local, bool split_limit) {
   if (request_local)
     hipLaunchKernelGGL(sched_kernel<true>, dim3(1), dim3(kSchedThreads), 0, stream, lengths, batch, num_parts, meta,
-                       num_splits);
+                       num_splits, split_limit ? 1 : 0);
   else
     hipLaunchKernelGGL(sched_kernel<false>, dim3(1), dim3(kSchedThreads), 0, stream, lengths, batch, num_parts, meta,
-                       num_splits);
+                       num_splits, split_limit ? 1 : 0);
   return hipGetLastError();
 }
 

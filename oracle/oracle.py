@@ -240,7 +240,9 @@ def pack_selected_kv(kcache_rec, indices, topk_length):
 # work went").  The partition rule itself is this library's reading, stated
 # here as a definition:
 #
-#   blocks_r = ceil(max(len_r, 0) / 64), T = sum_r blocks_r, P' = min(P, T).
+#   blocks_r = ceil(max(len_r, 0) / 64), T = sum_r blocks_r, P' = min(P, T, L)
+#   with L an optional split limit (the dense metadata call uses
+#   dense_split_limit below; the packed call uses none, L = T).
 #   Concatenate all requests' blocks in request order; part p < P' owns the
 #   global blocks [floor(p*T/P'), floor((p+1)*T/P')) (at least one block each),
 #   parts p >= P' own nothing.  A request's split count is the number of parts
@@ -248,20 +250,32 @@ def pack_selected_kv(kcache_rec, indices, topk_length):
 #   slots in part order, after the slots of all earlier requests.
 
 
-def sched_partition(lengths, num_parts):
+def dense_split_limit(batch, total_blocks):
+    """Split limit of the dense metadata call: at least 16 parts per request,
+    more when the requests are long (one part per 4 blocks), at most 64 per
+    request: max(16 b, min(ceil(T / 4), 64 b))."""
+    b, T = int(batch), int(total_blocks)
+    return max(16 * b, min(-(-T // 4), 64 * b))
+
+
+def sched_partition(lengths, num_parts, split_limit=None):
     """Plain-Python scheduler oracle.
 
     Returns (meta int32 [P, 8], num_splits int32 [b + 1]) with, per part:
       meta[p] = [begin_req, begin_blk, end_req, end_blk_exclusive, begin_split, 0, 0, 0]
     and begin_req = -1 (all fields -1 except the zeros) for a part that owns no
     block.  num_splits is the exclusive prefix sum of per-request split counts.
+    split_limit: "dense" for the dense metadata call's limit, None for none, or
+    an int.
     """
     lengths = [max(int(x), 0) for x in lengths]
     P = int(num_parts)
     assert P >= 1
     blocks = [(n + PAGE - 1) // PAGE for n in lengths]
     T = sum(blocks)
-    Pe = min(P, T)
+    if split_limit == "dense":
+        split_limit = dense_split_limit(len(lengths), T)
+    Pe = min(P, T) if split_limit is None else min(P, T, int(split_limit))
     # owner of every global block, found by scanning the part boundaries
     bounds = [(p * T) // Pe for p in range(Pe + 1)] if Pe else [0]
     owner = []

@@ -26,9 +26,10 @@ THRESHOLD = 8.0
 LOG2E = 1.0 / math.log(2.0)
 
 
-def pieces(lengths, num_parts):
-    """(request, first key, end key) of every piece, from the scheduler partition."""
-    meta, _ = O.sched_partition(lengths, num_parts)
+def pieces(lengths, num_parts, split_limit=None):
+    """(request, first key, end key) of every piece, from the scheduler partition
+    (split_limit "dense" for the dense metadata call's partition)."""
+    meta, _ = O.sched_partition(lengths, num_parts, split_limit=split_limit)
     out = []
     for br, bb, er, eb, _split in meta[:, :5]:
         if br < 0:
@@ -102,7 +103,7 @@ def moves_for(w, num_parts, margin=0.5):
     scorer = sparse_scores if w.fp8 else dense_scores
     cache = {}
     total = amb = 0
-    for r, lo, hi in pieces([int(x) for x in w.seqlens], num_parts):
+    for r, lo, hi in pieces([int(x) for x in w.seqlens], num_parts, None if w.fp8 else "dense"):
         if r not in cache:
             cache[r] = scorer(w, r)
         mv, am = count_moves(cache[r], lo, hi, margin=margin)

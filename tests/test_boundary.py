@@ -54,12 +54,12 @@ def test_decode_workspace_size_formula():
 
 @pytest.mark.parametrize("batch,s_q,h_q,cus,wgs,expect", [
     (64, 1, 128, 256, 1, 128),      # 64-row kernel: two row blocks per request -> 256 WG slots / 2
-    (1, 1, 128, 256, 1, 16),        # capped at 16 pieces per request
-    (8, 1, 64, 256, 1, 128),        # 64-row kernel, one row block: 8 requests x 16
+    (1, 1, 128, 256, 1, 64),        # capped at 64 pieces per request (the scheduler uses what the lengths need)
+    (8, 1, 64, 256, 1, 256),        # 64-row kernel, one row block: all 256 WG slots (cap 8 x 64)
     (16, 2, 128, 256, 1, 64),       # 256 rows: four row blocks per request -> 256 / 4
     (4, 4, 128, 256, 1, 32),        # 512 rows: eight row blocks, 256 / 8
-    (4, 1, 96, 256, 1, 64),         # 96 rows: two 64-row blocks (64-row kernel), 4 x 16
-    (1, 1, 16, 256, 1, 16),
+    (4, 1, 96, 256, 1, 128),        # 96 rows: two 64-row blocks (64-row kernel), 256 / 2
+    (1, 1, 16, 256, 1, 64),
     (1000, 1, 128, 256, 1, 128),
 ])
 def test_plan_num_parts(batch, s_q, h_q, cus, wgs, expect):
@@ -69,7 +69,7 @@ def test_plan_num_parts(batch, s_q, h_q, cus, wgs, expect):
 @pytest.mark.parametrize("fmt,batch,s_q,h_q,expect", [
     (ops.KV_FP8_PACKED, 8, 1, 64, 256),     # one row block per request; 32 pieces per request allowed
     (ops.KV_FP8_INDEXED, 2, 1, 128, 64),    # two row blocks: 128 slots, capped at 2 x 32
-    (ops.KV_BF16_PAGED, 8, 1, 64, 128),     # the bf16 kernel keeps 16 per request
+    (ops.KV_BF16_PAGED, 8, 1, 64, 256),     # the bf16 plan allows 64 per request
 ])
 def test_plan_num_parts_fp8_cap(fmt, batch, s_q, h_q, expect):
     assert ops.mla_plan_num_parts(batch, s_q, h_q, fmt, 256, 1) == expect
@@ -81,7 +81,7 @@ def test_plan_num_parts_multi_kv_head(batch, s_q, h_q, h_kv):
     mkv = s_q * (h_q // h_kv)
     rb = 16 * (1 if mkv <= 16 else 2 if mkv <= 32 else 4)
     row_blocks = h_kv * ((mkv + rb - 1) // rb)
-    want = min(max(256 // row_blocks, 1), batch * 16)
+    want = min(max(256 // row_blocks, 1), batch * 64)
     assert ops.mla_plan_num_parts(batch, s_q, h_q, ops.KV_BF16_PAGED, 256, 1, h_kv=h_kv) == want
 
 

@@ -343,18 +343,26 @@ def test_sparse_equals_dense_over_packed_records():
 
 # ----------------------------------------------------------------------------- scheduler partition
 
+@pytest.mark.parametrize("limit", [None, "dense"])
 @pytest.mark.parametrize("lengths,P", [
     ([4096] * 8, 32), ([4096] * 3, 7), ([1, 64, 65, 0, 300], 4), ([0, 0], 3), ([10], 5),
     ([2048, 4096, 3000, 100], 9), ([64] * 5, 5), ([128, 64], 1),
     ([1, 700, 2049], 64), ([300, 10, 0, 640], 50), ([4096], 256),   # more parts than blocks
+    ([65536], 128), ([16384], 128), ([65536, 64, 64, 64], 200),     # cut by the dense split limit
 ])
-def test_sched_partition_invariants(lengths, P):
-    meta, ns = O.sched_partition(lengths, P)
+def test_sched_partition_invariants(lengths, P, limit):
+    meta, ns = O.sched_partition(lengths, P, split_limit=limit)
     blocks = [(max(n, 0) + 63) // 64 for n in lengths]
     T = sum(blocks)
     cum = np.concatenate([[0], np.cumsum(blocks)])
+    P_all = P
+    if limit == "dense":
+        # the owner closed form below works with the number of parts in use
+        P = min(P, max(16 * len(lengths), min(-(-T // 4), 64 * len(lengths))))
     owned = np.zeros(T, int)
     sizes = []
+    assert meta.shape == (P_all, 8)
+    assert np.all(meta[P:, :5] == -1) and np.all(meta[P:, 5:] == 0)
     for p in range(P):
         br, bk, er, ek, bs = meta[p, :5]
         assert np.all(meta[p, 5:] == 0)
@@ -377,6 +385,16 @@ def test_sched_partition_invariants(lengths, P):
         expect = 0 if nb == 0 else brute.part_of(cum[r] + nb - 1, T, P) - brute.part_of(cum[r], T, P) + 1
         assert ns[r + 1] - ns[r] == expect
     assert ns[-1] <= sum(1 for x in blocks if x) + P - 1
+
+
+@pytest.mark.parametrize("b,T,want", [
+    (1, 16, 16), (1, 64, 16), (1, 65, 17), (1, 256, 64), (1, 1024, 64), (2, 1024, 128), (4, 257, 65),
+    (64, 4096, 1024), (16, 8192, 1024), (3, 45, 48), (1, 0, 16),
+])
+def test_dense_split_limit(b, T, want):
+    """The dense metadata call's split limit: 16 parts per request, one per 4
+    blocks beyond that, 64 per request at most (values worked by hand)."""
+    assert O.dense_split_limit(b, T) == want
 
 
 @pytest.mark.parametrize("lengths,P", [

@@ -41,7 +41,7 @@ def test_sched_metadata_bit_exact(lengths, P):
     seq = torch.tensor(np.asarray(lengths, np.int32), device="cuda:0")
     meta, ns = ops.mla_get_decode_metadata(seq, len(lengths), 1, 128, 1, P)
     torch.cuda.synchronize()
-    ref_meta, ref_ns = O.sched_partition(lengths, P)
+    ref_meta, ref_ns = O.sched_partition(lengths, P, split_limit="dense")
     assert np.array_equal(meta.cpu().numpy(), ref_meta)
     assert np.array_equal(ns.cpu().numpy(), ref_ns)
 
@@ -242,15 +242,21 @@ def test_batch_128_ragged_every_row():
     assert ops.mla_read_device_errors() == 0
 
 
-@pytest.mark.parametrize("parts", [128, 200])
-def test_combine_more_than_64_splits(parts):
-    """One request cut into more than 64 splits: the combine's lse reductions
-    run over several groups of 64."""
-    G.say(f"sk=16384 cut into {parts} splits")
-    w = W.dense_workload("many-splits", 197, 1, 1, 128, [16384], pool_pages=300, num_parts=parts)
+@pytest.mark.parametrize("parts,least", [(128, 64), (200, 128)])
+def test_combine_more_than_64_splits(parts, least):
+    """One request cut into more than 64 splits (a 65536-token request next to
+    three one-page ones, so that the split limit allows up to 64 parts per
+    request on average): the combine's lse reductions run over several groups
+    of 64."""
+    lengths = [65536, 64, 64, 64]
+    G.say(f"lengths {lengths} in {parts} parts")
+    w = W.dense_workload("many-splits", 197, 4, 1, 128, lengths, pool_pages=1040, num_parts=parts)
     out, lse, plan = G.run_dense(w)
-    splits = int(plan.num_splits.cpu().numpy()[1])
-    assert splits == parts > 64
+    ns = plan.num_splits.cpu().numpy()
+    assert np.array_equal(ns, O.sched_partition(lengths, parts, split_limit="dense")[1])
+    splits = int(ns[1])
+    G.say(f"  request 0 in {splits} splits")
+    assert splits > least
     G.compare(f"splits{parts}", out, lse, *oracle_dense(w))
 
 
