@@ -552,12 +552,12 @@ def profile_loop(args):
         ws = ops.mla_pack_selected_kv(rec, idx, tl)
         calls = [ops.mla_pack_selected_kv(rec, idx, tl, ws, bind=True)]
         for fmt in (ops.KV_FP8_PACKED, ops.KV_FP8_INDEXED):
-            p = ops.DecodePlan(tl, s_q, h_q, fmt)
+            p = ops.DecodePlan(tl, s_q, h_q, fmt, topk_capacity=cap)
             out = torch.empty((b, s_q, h_q, 512), dtype=torch.bfloat16, device=dev)
             lse = torch.empty((b, s_q, h_q), dtype=torch.float32, device=dev)
             kv, ix = (ws, None) if fmt == ops.KV_FP8_PACKED else (rec, idx)
-            calls += [ops.mla_get_decode_metadata(tl, b, s_q, h_q, 1, p.num_parts, p.sched_meta, p.num_splits,
-                                                  bind=True),
+            calls += [ops.mla_get_packed_decode_metadata(tl, b, s_q, h_q, cap, p.num_parts, ops.SCHED_AUTO,
+                                                         p.sched_meta, p.num_splits, bind=True),
                       ops.mla_decode_fwd(q, kv, fmt, ix, tl, w.scale, False, p.sched_meta, p.num_splits, out, lse,
                                          p.workspace, topk_capacity=cap, bind=True),
                       ops.mla_combine(p.num_splits, p.workspace, b, s_q, h_q, p.num_parts, out, lse, bind=True)]
@@ -712,7 +712,8 @@ def _sparse_case_line(torch, ops, w, dev, stream, flush, reps, copy_gbs, oracle=
         out = torch.empty((b, s_q, h_q, 512), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((b, s_q, h_q), dtype=torch.float32, device=dev)
         kv, ix = (ws, None) if fmt == ops.KV_FP8_PACKED else (rec, idx)
-        calls[key] = [ops.mla_get_decode_metadata(tl, b, s_q, h_q, 1, parts, meta, ns, bind=True),
+        calls[key] = [ops.mla_get_packed_decode_metadata(tl, b, s_q, h_q, cap, parts, ops.SCHED_AUTO, meta, ns,
+                                                         bind=True),
                       ops.mla_decode_fwd(q, kv, fmt, ix, tl, w.scale, False, meta, ns, out, lse, pws,
                                          topk_capacity=cap, bind=True),
                       ops.mla_combine(ns, pws, b, s_q, h_q, parts, out, lse, bind=True)]
@@ -861,15 +862,14 @@ def sparse_main(args):
         ids = t["indices"][:, 0, :1].contiguous()  # one selected current token per request
         out = torch.empty((b, s_q, h_q, 512), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((b, s_q, h_q), dtype=torch.float32, device=dev)
-        plans = {f: ops.DecodePlan(t["seqlens"], s_q, h_q, f) for f in (ops.KV_FP8_INDEXED, ops.KV_FP8_PACKED)}
+        plans = {f: ops.DecodePlan(t["seqlens"], s_q, h_q, f, topk_capacity=cap)
+                 for f in (ops.KV_FP8_INDEXED, ops.KV_FP8_PACKED)}
 
         def decode(fmt, policy=None):
             p = plans[fmt]
-            if policy is None:
-                ops.mla_get_decode_metadata(t["seqlens"], b, s_q, h_q, 1, p.num_parts, p.sched_meta, p.num_splits)
-            else:
-                ops.mla_get_packed_decode_metadata(t["seqlens"], b, s_q, h_q, cap, p.num_parts, policy, p.sched_meta,
-                                                   p.num_splits)
+            ops.mla_get_packed_decode_metadata(t["seqlens"], b, s_q, h_q, cap, p.num_parts,
+                                               ops.SCHED_AUTO if policy is None else policy, p.sched_meta,
+                                               p.num_splits)
             kv, ix = (t["kcache_rec"], t["indices"]) if fmt == ops.KV_FP8_INDEXED else (ws, None)
             ops.mla_decode_fwd(t["q"], kv, fmt, ix, t["seqlens"], w.scale, False, p.sched_meta, p.num_splits, out,
                                lse, p.workspace, topk_capacity=cap)

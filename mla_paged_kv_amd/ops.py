@@ -341,12 +341,20 @@ class DecodePlan:
     Built once per step (the metadata depends only on the lengths) and reused by
     every layer of that step, as the scheduler metadata is meant to be."""
 
-    def __init__(self, seqlens, s_q, h_q, kv_format=KV_BF16_PAGED, num_parts=None, stream=None, h_kv=1):
+    def __init__(self, seqlens, s_q, h_q, kv_format=KV_BF16_PAGED, num_parts=None, stream=None, h_kv=1,
+                 topk_capacity=None):
         b = seqlens.shape[0]
         self.batch, self.s_q, self.h_q, self.kv_format = b, s_q, h_q, kv_format
         self.num_parts = int(num_parts) if num_parts else mla_decode_num_parts(b, s_q, h_q, h_kv, kv_format)
-        self.sched_meta, self.num_splits = mla_get_decode_metadata(seqlens, b, s_q, h_q, 1, self.num_parts,
-                                                                   stream=stream)
+        if kv_format in (KV_FP8_PACKED, KV_FP8_INDEXED):
+            # the sparse paths' own scheduler call (seqlens = topk_length)
+            if not topk_capacity:
+                raise ValueError("DecodePlan: the FP8 formats need topk_capacity")
+            self.sched_meta, self.num_splits = mla_get_packed_decode_metadata(
+                seqlens, b, s_q, h_q, int(topk_capacity), self.num_parts, stream=stream)
+        else:
+            self.sched_meta, self.num_splits = mla_get_decode_metadata(seqlens, b, s_q, h_q, 1, self.num_parts,
+                                                                       stream=stream)
         nbytes = mla_decode_workspace_size(b, s_q, h_q, self.num_parts)
         self.workspace = torch.empty((nbytes,), dtype=torch.uint8, device=seqlens.device)
 
@@ -359,7 +367,7 @@ def mla_decode(q, kv, block_table, seqlens, softmax_scale=None, causal=False, pl
         softmax_scale = 1.0 / math.sqrt(D_QK)
     if plan is None:
         h_kv = kv.shape[2] if kv_format in (KV_BF16_PAGED, KV_FP16_PAGED) else 1
-        plan = DecodePlan(seqlens, s_q, h_q, kv_format, stream=stream, h_kv=h_kv)
+        plan = DecodePlan(seqlens, s_q, h_q, kv_format, stream=stream, h_kv=h_kv, topk_capacity=topk_capacity)
     if out is None:
         out = torch.empty((b, s_q, h_q, D_V), dtype=_act_dtype(kv_format), device=q.device)
     if lse is None:

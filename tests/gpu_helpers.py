@@ -47,7 +47,8 @@ def run_dense(w, t=None, num_parts=None):
 def run_sparse(w, t=None, num_parts=None):
     t = t or dev_tensors(w)
     ws = ops.mla_pack_selected_kv(t["kcache_rec"], t["indices"], t["seqlens"])
-    plan = ops.DecodePlan(t["seqlens"], w.s_q, w.h_q, ops.KV_FP8_PACKED, num_parts=num_parts or w.num_parts)
+    plan = ops.DecodePlan(t["seqlens"], w.s_q, w.h_q, ops.KV_FP8_PACKED, num_parts=num_parts or w.num_parts,
+                          topk_capacity=w.topk_capacity)
     out, lse = ops.mla_decode(t["q"], ws, None, t["seqlens"], w.scale, False, plan=plan,
                               kv_format=ops.KV_FP8_PACKED, topk_capacity=w.topk_capacity)
     torch.cuda.synchronize()
@@ -58,7 +59,8 @@ def run_sparse_indexed(w, t=None, num_parts=None):
     """Sparse FP8 decode straight from the record pool (records gathered by
     top-k id inside the decode, no pack)."""
     t = t or dev_tensors(w)
-    plan = ops.DecodePlan(t["seqlens"], w.s_q, w.h_q, ops.KV_FP8_INDEXED, num_parts=num_parts or w.num_parts)
+    plan = ops.DecodePlan(t["seqlens"], w.s_q, w.h_q, ops.KV_FP8_INDEXED, num_parts=num_parts or w.num_parts,
+                          topk_capacity=w.topk_capacity)
     out, lse = ops.mla_decode(t["q"], t["kcache_rec"], t["indices"], t["seqlens"], w.scale, False, plan=plan,
                               kv_format=ops.KV_FP8_INDEXED, topk_capacity=w.topk_capacity)
     torch.cuda.synchronize()

@@ -651,7 +651,7 @@ def test_patch_after_early_pack(side_stream):
     ref_ws = O.pack_selected_kv(new_pool, w.indices, w.seqlens)
     assert not np.array_equal(ref_ws, O.pack_selected_kv(w.kcache_rec, w.indices, w.seqlens))  # the patch matters
     assert np.array_equal(ws.cpu().numpy(), ref_ws.reshape(-1))
-    plan = ops.DecodePlan(t["seqlens"], w.s_q, w.h_q, ops.KV_FP8_PACKED)
+    plan = ops.DecodePlan(t["seqlens"], w.s_q, w.h_q, ops.KV_FP8_PACKED, topk_capacity=w.topk_capacity)
     out_p, lse_p = ops.mla_decode(t["q"], ws, None, t["seqlens"], w.scale, False, plan=plan,
                                   kv_format=ops.KV_FP8_PACKED, topk_capacity=w.topk_capacity)
     out_i, lse_i = ops.mla_decode(t["q"], t["kcache_rec"], t["indices"], t["seqlens"], w.scale, False, plan=plan,
@@ -823,7 +823,7 @@ def test_no_writes_outside_the_buffers(fmt):
         cap = 0
     else:
         cap = w.topk_capacity
-        ops.mla_get_decode_metadata(t["seqlens"], b, s_q, h_q, 1, P, meta, ns)
+        ops.mla_get_packed_decode_metadata(t["seqlens"], b, s_q, h_q, cap, P, ops.SCHED_AUTO, meta, ns)
         if fmt == "packed":
             pw, pws = _padded(ops.mla_packed_kv_workspace_size(b, s_q, cap), torch.uint8, 0xA5)
             ops.mla_pack_selected_kv(t["kcache_rec"], t["indices"], t["seqlens"], pws)
