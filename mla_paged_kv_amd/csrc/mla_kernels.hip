@@ -539,21 +539,51 @@ struct TileLoader<true> {
 // idx = indices[row][key0 + j] (row = r * s_q + s for query token s of request
 // r).  One wave-wide load per record (lanes 0..40 each move one 16-byte chunk
 // of the 656 bytes; the others idle), so the record's base address is
-// wave-uniform and comes from a scalar load of its index; wave w moves records
-// w, w + 4, ..., w + 28 into the same raw tile layout the packed loader
-// produces.  Keys past the request's top-k length `n` (set per request, already
-// clamped to the capacity) load record 0 (they are masked); an index of the
-// valid prefix outside the pool is flagged and replaced by 0.
+// wave-uniform; wave w moves records w, w + 4, ..., w + 28 into the same raw
+// tile layout the packed loader produces.  The ids of a request piece's first
+// kIdxCache keys are staged in LDS when the piece starts: one LDS read then
+// gives lane k the id of the wave's k-th record and the bases are formed on
+// the scalar unit (an id read per record on the tile's critical path cost
+// about 1.3 us per tile); later keys read their ids with scalar loads.  Keys
+// past the request's top-k length `n` (set per request, already clamped to the
+// capacity) load record 0 (they are masked); an index of the valid prefix
+// outside the pool is flagged and replaced by 0.
 constexpr int kIdxLoadsPerWave = kTK / 4;  // 8
+constexpr int kIdxCache = 2048;            // top-k ids of a request piece staged in LDS
+constexpr int kF8OffIdsLoader = 139072;    // = kF8OffIds (checked below)
 struct IndexedLoader {
   static constexpr int kLoads = kIdxLoadsPerWave;
   int n = 0;
+  int kc0 = 0, kc1 = 0;  // keys [kc0, kc1) of the current row have their ids staged in LDS
   __device__ void init(int, int) {}
   __device__ static int loads_of_wave(int) { return kIdxLoadsPerWave; }
   __device__ void issue(const DecodeArgs& a, int row, int key0, LDS_AS uint8_t* smem, int st, int w) const {
     const int l = threadIdx.x & 63;
     const int64_t limit = a.num_pages * kPage;
     LDS_AS uint8_t* dst = smem + kOffRaw + st * kRawTileBytes;
+    if (key0 >= kc0 && key0 + kTK <= kc1) {
+      // ids staged in LDS (one cold round trip per request piece, not per tile):
+      // one read gives lane k the id of record w + 4k, and the record bases
+      // are then formed on the scalar unit
+      const LDS_AS int32_t* ids = reinterpret_cast<const LDS_AS int32_t*>(smem + kF8OffIdsLoader);
+      int rec = w + 4 * (l & 7);
+      asm volatile("" : "+v"(rec));  // the LDS address is formed here, not hoisted (and spilled)
+      const int v = key0 + rec < n ? ids[key0 - kc0 + rec] : 0;
+      bool bad = false;
+#pragma unroll
+      for (int k = 0; k < kIdxLoadsPerWave; ++k) {
+        int64_t idx = __builtin_amdgcn_readlane(v, k);
+        if (idx < 0 || idx >= limit) {
+          bad = true;
+          idx = 0;
+        }
+        const uint64_t base = uniform_u64((uint64_t)(uintptr_t)a.kv + (uint64_t)idx * kRecBytes);
+        if (l < kRecBytes / 16) load_lds16_s(base, 16u * (uint32_t)l, dst + (w + 4 * k) * kRecBytes);
+      }
+      if (bad && l == 0) atomicOr(&g_error_flags, kErrIndex);
+      return;
+    }
+    // keys past the staged range: one scalar id read per record
 #pragma unroll
     for (int k = 0; k < kIdxLoadsPerWave; ++k) {
       const int j = w + 4 * k;
@@ -1129,7 +1159,10 @@ constexpr int kF8OffAlpha = kF8OffS + kStages * 4 * kTK * 4;             // 1382
 constexpr int kF8OffFlag = kF8OffAlpha + 2 * kMaxRowsPerWG * 4;          // 138752
 constexpr int kF8OffL = kF8OffFlag + 64;                                 // 138816
 constexpr int kF8LdsBytes = kF8OffL + kMaxRowsPerWG * 4;                 // 139072
-static_assert(kF8LdsBytes <= 160 * 1024, "FP8 wave-specialised LDS budget");
+constexpr int kF8OffIds = kF8LdsBytes;                                    // by index: top-k ids of the piece
+constexpr int kF8LdsBytesIdx = kF8OffIds + kIdxCache * 4;                 // 147264
+static_assert(kF8OffIds == kF8OffIdsLoader, "indexed loader's id cache offset");
+static_assert(kF8LdsBytesIdx <= 160 * 1024, "FP8 wave-specialised LDS budget");
 static_assert(kF8OffC % 16 == 0 && kF8OffP % 16 == 0 && kF8OffS % 16 == 0, "16-B aligned LDS regions");
 
 // 8 E4M3 bytes (two dwords, byte k = element k) -> 8 bf16, exactly
@@ -1182,7 +1215,7 @@ template <bool IDX>
 __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs a) {
   constexpr int RB = 4, MB = 64;
   using Loader = std::conditional_t<IDX, IndexedLoader, TileLoader<true>>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[kF8LdsBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[IDX ? kF8LdsBytesIdx : kF8LdsBytes];
   LDS_AS uint8_t* smem = (LDS_AS uint8_t*)(smem_raw);
   LDS_AS uint8_t* cvt = smem + kF8OffC;
   LDS_AS float* scales_s = reinterpret_cast<LDS_AS float*>(smem + kF8OffS);     // [4 tiles][4 blocks][32 keys]
@@ -1250,6 +1283,16 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
     }
     const int rho = rbk * MB + row_local;
     auto raw_slot = [&](int t) -> LDS_AS uint8_t* { return smem + kOffRaw + (t & 3) * kRawTileBytes; };
+    if constexpr (IDX) {
+      // the piece's first kIdxCache top-k ids -> LDS, read by the ring loads
+      // (later ids, if any, are read directly)
+      LDS_AS int32_t* ids = reinterpret_cast<LDS_AS int32_t*>(smem + kF8OffIds);
+      const int kc1 = max(min(t1, t0 + kIdxCache), t0);
+      for (int i = tid; i < kc1 - t0; i += kWsThreads) ids[i] = a.block_table[(int64_t)lrow * a.cap + t0 + i];
+      loader.kc0 = t0;
+      loader.kc1 = kc1;
+      sync_lds();
+    }
 
     if (is_qk) {
       // ================================================================ QK waves
@@ -1404,8 +1447,13 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
             l_s[row_local] = lt;
             if (rho < a.M) {
               const float lse = lt > 0.f ? (mrow + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
-              if (nsplit == 1) a.lse[(int64_t)r * a.M + rho] = lse;
-              else a.part_lse[(int64_t)slot * a.M + rho] = lse;
+              // by index, the row index is made opaque: otherwise the compiler
+              // hoists the 64-bit store addresses out of the request loop and
+              // spills them
+              int gr = rho;
+              if constexpr (IDX) asm volatile("" : "+v"(gr));
+              if (nsplit == 1) a.lse[(int64_t)r * a.M + gr] = lse;
+              else a.part_lse[(int64_t)slot * a.M + gr] = lse;
             }
           }
         }
@@ -1505,8 +1553,9 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
       sync_lds();  // l from the QK waves (written in iteration ntile)
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const int rho_o = rbk * MB + 16 * rb + li;
+        int rho_o = rbk * MB + 16 * rb + li;
         if (rho_o >= a.M) continue;
+        if constexpr (IDX) asm volatile("" : "+v"(rho_o));  // keeps the row addresses from being hoisted and spilled
         const float lt = l_s[16 * rb + li];
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         if (nsplit == 1) {
