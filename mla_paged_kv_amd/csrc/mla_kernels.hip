@@ -1131,22 +1131,24 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
 // exactly (every E4M3 value is a bf16 value) and the per-key fp32 block scales
 // are applied in fp32 to the scores and to P, never to a rounded K or V.
 //   * Each tile's NoPE K is converted once, into a shared bf16 buffer: at the
-//     start of iteration t each QK wave converts a quarter of raw tile t (and
+//     start of iteration t every wave converts an eighth of raw tile t (and
 //     zeroes the NoPE bytes of its records past the valid count, which the PV
-//     waves read next iteration), then every wave passes a barrier.
+//     waves read next iteration), then every wave passes a barrier.  (With the
+//     conversion in the QK waves alone it sat on their critical path: the
+//     decode at b=64, h_q=128, top-k 2048 took 69.2 us against 65.3.)
 //   * QK waves 0..3 (16 rows each) then compute S(t)^T = K(t) Q^T like the bf16
 //     kernel, K operands from the converted buffer (NoPE) and the raw records
 //     (RoPE, already bf16).  The four 128-dim NoPE blocks and the RoPE part
 //     accumulate apart, and each key's block scales combine them at the end of
-//     the tile.  The softmax of tile t-1 runs between the k-steps of tile t;
-//     P(t-1) is written four times, multiplied by each key's scale of NoPE
-//     block b for the PV waves of block b.  They also stream the ring.
+//     the tile.  The softmax of tile t-1 runs between the k-steps of tile t and
+//     writes P(t-1) once, unnormalised, in fp32.  They also stream the ring.
 //   * PV waves 4..7: wave 4+w owns output columns [128w, 128w+128) -- NoPE
-//     block w -- for all rows.  V^T fragments come from ds_read_b64_tr_b8 on the
-//     raw records (in a 16-lane group, lane j addresses key 8g + j/2 at byte
-//     8 (j & 1) of the 16 columns; lane i receives column i of keys 8g ..
-//     8g+7), converted in registers.  Half of their MFMAs run before the
-//     conversion barrier, half after.
+//     block w -- for all rows.  After the conversion barrier they read P(t-2),
+//     multiply it by each key's scale of block w and round it to bf16 (their
+//     P^T operand), and compute O += V^T P^T.  V^T fragments come from
+//     ds_read_b64_tr_b8 on the raw records (in a 16-lane group, lane j
+//     addresses key 8g + j/2 at byte 8 (j & 1) of the 16 columns; lane i
+//     receives column i of keys 8g .. 8g+7), converted in registers.
 // Two barriers per tile; the ring holds 4 raw tiles (2 in flight), as in the
 // bf16 kernel.  64 rows per workgroup (h_q is 64 or 128 on these paths).
 constexpr int kCvtPitch = 1024 + 32;  // converted NoPE row: 512 bf16 + 32 B (16-row reads conflict-free)
@@ -1182,32 +1184,33 @@ __device__ __forceinline__ u32x2 lds_read_tr8(const LDS_AS uint8_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// Converts the NoPE bytes of keys [8w, 8w + 8) of a raw tile into the bf16
-// buffer (row k at k * kCvtPitch), copies their four block scales into the
-// tile's scale table (scale b of key k at 32 b + k), and zeroes, in the raw
-// tile, the NoPE bytes of those keys at or past `nvalid`: they score -inf and
-// get P = 0, but 0 * NaN would still poison PV if such a record decodes to NaN
-// (the by-index loader reads record 0 for them).  Lane l handles 8-byte units
-// (l & 7) + 8 j, j < 8, of key 8w + (l >> 3): each group of 8 lanes writes 128
-// contiguous bytes.
-__device__ __forceinline__ void convert_nope_quarter(LDS_AS uint8_t* raw, LDS_AS uint8_t* cvt, LDS_AS float* scales,
-                                                     int w, int nvalid) {
-  const int l = threadIdx.x & 63;
-  const int key = 8 * w + (l >> 3);
-  LDS_AS uint8_t* src = raw + key * kRecBytes + 8 * (l & 7);
-  LDS_AS uint8_t* dst = cvt + key * kCvtPitch + 16 * (l & 7);
-  u32x2 v[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const LDS_AS u32x2*>(src + 64 * j);
+// Converts the NoPE bytes of keys [4v, 4v + 4) of a raw tile (v = 0..7: every
+// wave of the workgroup converts an eighth) into the bf16 buffer (row k at
+// k * kCvtPitch), copies their four block scales into the tile's scale table
+// (scale b of key k at 32 b + k), and zeroes, in the raw tile, the NoPE bytes
+// of those keys at or past `nvalid`: they score -inf and get P = 0, but 0 * NaN
+// would still poison PV if such a record decodes to NaN (the by-index loader
+// reads record 0 for them).  Lane l handles 8-byte units (l & 15) + 16 j, j < 4,
+// of key 4v + (l >> 4): each group of 16 lanes writes 256 contiguous bytes.
+__device__ __forceinline__ void convert_nope_eighth(LDS_AS uint8_t* raw, LDS_AS uint8_t* cvt, LDS_AS float* scales,
+                                                    int v8, int nvalid) {
+  int l = threadIdx.x & 63;
+  asm volatile("" : "+v"(l));  // addresses formed here, not hoisted out of the tile loop (and spilled)
+  const int key = 4 * v8 + (l >> 4);
+  LDS_AS uint8_t* src = raw + key * kRecBytes + 8 * (l & 15);
+  LDS_AS uint8_t* dst = cvt + key * kCvtPitch + 16 * (l & 15);
   float sc = 0.f;
-  const int skey = 8 * w + ((l >> 2) & 7), sb = l & 3;
-  if (l < 32) sc = *reinterpret_cast<const LDS_AS float*>(raw + skey * kRecBytes + 512 + 4 * sb);
+  const int skey = 4 * v8 + ((l >> 2) & 3), sb = l & 3;
+  if (l < 16) sc = *reinterpret_cast<const LDS_AS float*>(raw + skey * kRecBytes + 512 + 4 * sb);
+  u32x2 v[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) *reinterpret_cast<LDS_AS bf16x8*>(dst + 128 * j) = e4m3x8_to_bf16(v[j]);
-  if (l < 32) scales[32 * sb + skey] = sc;
+  for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<const LDS_AS u32x2*>(src + 128 * j);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) *reinterpret_cast<LDS_AS bf16x8*>(dst + 256 * j) = e4m3x8_to_bf16(v[j]);
+  if (l < 16) scales[32 * sb + skey] = sc;
   if (nvalid < kTK && key >= nvalid) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) *reinterpret_cast<LDS_AS u32x2*>(src + 64 * j) = u32x2{0u, 0u};
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<LDS_AS u32x2*>(src + 128 * j) = u32x2{0u, 0u};
   }
 }
 
@@ -1427,9 +1430,9 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
         constexpr bool DO_SM = decltype(do_sm_c)::value;
         const bool more = t + 2 < ntile;
         if (more) loader.issue(a, lrow, t0 + (t + 2) * kTK, smem, (t + 2) & 3, w);
-        if constexpr (DO_QK)
-          convert_nope_quarter(raw_slot(t), cvt, scales_s + (t & 3) * 4 * kTK, w, min(kTK, t1 - (t0 + t * kTK)));
-        sync_lds();  // tile t's NoPE K converted
+        if (t < ntile)
+          convert_nope_eighth(raw_slot(t), cvt, scales_s + (t & 3) * 4 * kTK, w, min(kTK, t1 - (t0 + t * kTK)));
+        sync_lds();  // tile t's NoPE K converted (by all eight waves)
         if constexpr (DO_QK) {
           if constexpr (DO_SM) {
             // the softmax of t-1 reads sx, which qk(t) overwrites only at its end
@@ -1492,6 +1495,9 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
         constexpr bool DO_PV = decltype(do_pv_c)::value;
         constexpr bool DO_VREAD = decltype(do_vread_c)::value;
         const int tp = t - 2;
+        if (t < ntile)
+          convert_nope_eighth(raw_slot(t), cvt, scales_s + (t & 3) * 4 * kTK, 4 + w, min(kTK, t1 - (t0 + t * kTK)));
+        sync_lds();  // the conversion barrier
         uint32_t fl = 0;
         float al[RB];
         bf16x8 bp[RB];
@@ -1536,7 +1542,6 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
           }
         };
         blocks(0);
-        sync_lds();  // the QK waves' conversion barrier
         blocks(4);
         sync_lds();
       };
