@@ -78,7 +78,7 @@ constexpr float kRescaleThreshold = 8.0f;           // log2 units: p <= 2^8 betw
 // LDS layout
 constexpr int kPBufBytes = kMaxRowsPerWG * kPStride;            // one P buffer (6 KB)
 constexpr int kOffKDense = 0;
-constexpr int kOffRaw = 0;                                      // FP8: raw ring
+constexpr int kOffRaw = 2 * kTileBytes;                        // FP8: raw ring, after two bf16 tiles
 
 // ------------------------------------------------------------------ small device helpers
 template <int N>
@@ -200,6 +200,15 @@ __device__ __forceinline__ float row4_sum(float v) {
 // byte offset of (key row kr, 16-B chunk c) inside a swizzled bf16 tile
 __device__ __forceinline__ uint32_t tile_off(int kr, int c) {
   return (uint32_t)(kr * kRowBytes + ((c ^ (kr & 7)) << 4));
+}
+
+// Lane id in [0, 64), computed where it is used: the asm is never hoisted, so
+// values derived from it do not stay live (and spill) across the tile loops.
+// Every lane of the wave must be active.
+__device__ __forceinline__ int lane_id_here() {
+  int v;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
+  return v;
 }
 
 // ------------------------------------------------------------------ scheduler
@@ -563,8 +572,8 @@ struct TileLoader<true> {
 // capacity) load record 0 (they are masked); an index of the valid prefix
 // outside the pool is flagged and replaced by 0.
 constexpr int kIdxLoadsPerWave = kTK / 4;  // 8
-constexpr int kIdxCache = 2048;            // top-k ids of a request piece staged in LDS
-constexpr int kF8OffIdsLoader = 139072;    // = kF8OffIds (checked below)
+constexpr int kIdxCache = 1024;            // top-k ids of a request piece staged in LDS
+constexpr int kF8OffIdsLoader = 159040;    // = kF8OffIds (checked below)
 struct IndexedLoader {
   static constexpr int kLoads = kIdxLoadsPerWave;
   int n = 0;
@@ -1141,45 +1150,50 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
 // ------------------------------------------------------------------ FP8 decode, wave-specialised
 //
 // The sparse FP8 paths with the two-role structure of decode_ws_kernel.  The raw
-// 656-byte records stream into a ring; E4M3 values are converted to bf16
-// exactly (every E4M3 value is a bf16 value) and the per-key fp32 block scales
-// are applied in fp32 to the scores and to P, never to a rounded K or V.
-//   * Each tile's NoPE K is converted once, into a shared bf16 buffer: at the
-//     start of iteration t every wave converts an eighth of raw tile t (and
-//     zeroes the NoPE bytes of its records past the valid count, which the PV
-//     waves read next iteration), then every wave passes a barrier.  (With the
-//     conversion in the QK waves alone it sat on their critical path: the
-//     decode at b=64, h_q=128, top-k 2048 took 69.2 us against 65.3.)
-//   * QK waves 0..3 (16 rows each) then compute S(t)^T = K(t) Q^T like the bf16
-//     kernel, K operands from the converted buffer (NoPE) and the raw records
-//     (RoPE, already bf16).  The four 128-dim NoPE blocks and the RoPE part
-//     accumulate apart, and each key's block scales combine them at the end of
-//     the tile.  The softmax of tile t-1 runs between the k-steps of tile t and
-//     writes P(t-1) once, unnormalised, in fp32.  They also stream the ring.
+// 656-byte records stream into a 3-slot ring.  One iteration ahead of their use,
+// the PV waves convert each raw tile into a bf16 tile in the dense kernel's
+// swizzled layout (E4M3 -> bf16 is exact: every E4M3 value is a bf16 value; the
+// RoPE part is copied) and copy the per-key fp32 block scales into two tables.
+// The scales are applied in fp32 to the scores and to P, never to a rounded K
+// or V.
+//   * QK waves 0..3 (16 rows each): S(t)^T = K(t) Q^T from bf16 tile t & 1 with
+//     the dense kernel's operand reads.  The four 128-dim NoPE blocks and the
+//     RoPE part accumulate apart, and each key's block scales combine them at
+//     the end of the tile.  The softmax of tile t-1 runs between the k-steps of
+//     tile t and writes P(t-1) once, unnormalised, in fp32.  They also stream
+//     the ring: raw tile t+3 at the start of iteration t, into the slot of raw
+//     tile t (converted in iteration t-1).
 //   * PV waves 4..7: wave 4+w owns output columns [128w, 128w+128) -- NoPE
-//     block w -- for all rows.  After the conversion barrier they read P(t-2),
-//     multiply it by each key's scale of block w and round it to bf16 (their
-//     P^T operand), and compute O += V^T P^T.  V^T fragments come from
-//     ds_read_b64_tr_b8 on the raw records (in a 16-lane group, lane j
-//     addresses key 8g + j/2 at byte 8 (j & 1) of the 16 columns; lane i
-//     receives column i of keys 8g .. 8g+7), converted in registers.
-// Two barriers per tile; the ring holds 4 raw tiles (2 in flight), as in the
-// bf16 kernel.  64 rows per workgroup (h_q is 64 or 128 on these paths).
-constexpr int kCvtPitch = 1024 + 32;  // converted NoPE row: 512 bf16 + 32 B (16-row reads conflict-free)
-constexpr int kF8PPitch = kTK * 4 + 16;  // fp32 P row: 32 keys + 16 B
-constexpr int kF8PBuf = kMaxRowsPerWG * kF8PPitch;                       // 9216
-constexpr int kF8OffC = kStages * kRawTileBytes;                         // 83968: converted NoPE K, 32 rows
-constexpr int kF8OffP = kF8OffC + kTK * kCvtPitch;                       // 117760: fp32 P[2 parities]
-constexpr int kF8OffS = kF8OffP + 2 * kF8PBuf;                           // 136192: block scales [4 tiles][4][32]
-constexpr int kF8OffAlpha = kF8OffS + kStages * 4 * kTK * 4;             // 138240
-constexpr int kF8OffFlag = kF8OffAlpha + 2 * kMaxRowsPerWG * 4;          // 138752
-constexpr int kF8OffL = kF8OffFlag + 64;                                 // 138816
-constexpr int kF8LdsBytes = kF8OffL + kMaxRowsPerWG * 4;                 // 139072
-constexpr int kF8OffIds = kF8LdsBytes;                                    // by index: top-k ids of the piece
-constexpr int kF8LdsBytesIdx = kF8OffIds + kIdxCache * 4;                 // 147264
+//     block w -- for all rows.  In iteration t it reads P(t-2), multiplies it by
+//     each key's scale of block w and rounds it to bf16 (its P^T operand),
+//     computes O += V(t-2)^T P^T from registers while reading V(t-1) into them
+//     (transposed reads as in the dense kernel), and then converts block w of
+//     raw tile t+1, for all 32 keys, into bf16 tile (t+1) & 1: exactly the
+//     region its own V(t-1) reads have just left (a wave's LDS accesses complete
+//     in order).  It also copies an eighth of that tile's RoPE and its block-w
+//     scales.  Keys past the tile's valid count get zeros (K, V and scales), so
+//     no record outside the valid prefix reaches the result (the by-index
+//     loader reads record 0 for them).
+// One barrier per tile.  (The earlier version converted tile t at the start of
+// iteration t in all eight waves, behind a second barrier, and converted V in
+// registers after ds_read_b64_tr_b8 reads of the raw records: the conversion
+// and that barrier sat on the QK waves' path every tile.)
+constexpr int kF8RawSlots = 3;
+constexpr int kF8PPitch = kTK * 4 + 16;                          // fp32 P row: 32 keys + 16 B
+constexpr int kF8PBuf = kMaxRowsPerWG * kF8PPitch;               // 9216
+constexpr int kF8OffP = kOffRaw + kF8RawSlots * kRawTileBytes;   // 136704: fp32 P[2 parities]
+constexpr int kF8OffS = kF8OffP + 2 * kF8PBuf;                   // 155136: PV scales [4 tiles][4 blocks][32 keys]
+constexpr int kF8OffSq = kF8OffS + 4 * 4 * kTK * 4;              // 157184: QK scales [2 tiles][32 keys][4 blocks]
+constexpr int kF8OffAlpha = kF8OffSq + 2 * kTK * 4 * 4;          // 158208
+constexpr int kF8OffFlag = kF8OffAlpha + 2 * kMaxRowsPerWG * 4;  // 158720
+constexpr int kF8OffL = kF8OffFlag + 64;                         // 158784
+constexpr int kF8LdsBytes = kF8OffL + kMaxRowsPerWG * 4;         // 159040
+constexpr int kF8OffIds = kF8LdsBytes;                           // by index: top-k ids of the piece
+constexpr int kF8LdsBytesIdx = kF8OffIds + kIdxCache * 4;        // 163136
+static_assert(kOffRaw == 2 * kTileBytes, "FP8 raw ring after the two bf16 tiles");
 static_assert(kF8OffIds == kF8OffIdsLoader, "indexed loader's id cache offset");
 static_assert(kF8LdsBytesIdx <= 160 * 1024, "FP8 wave-specialised LDS budget");
-static_assert(kF8OffC % 16 == 0 && kF8OffP % 16 == 0 && kF8OffS % 16 == 0, "16-B aligned LDS regions");
+static_assert(kF8OffP % 16 == 0 && kF8OffS % 16 == 0 && kF8OffSq % 16 == 0, "16-B aligned LDS regions");
 
 // 8 E4M3 bytes (two dwords, byte k = element k) -> 8 bf16, exactly
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 raw) {
@@ -1191,41 +1205,48 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 raw) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-__device__ __forceinline__ u32x2 lds_read_tr8(const LDS_AS uint8_t* p) {
-  typedef int i32x2_t __attribute__((ext_vector_type(2)));
-  const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-      reinterpret_cast<LDS_AS i32x2_t*>(const_cast<LDS_AS uint8_t*>(p)));
-  return __builtin_bit_cast(u32x2, v);
-}
-
-// Converts the NoPE bytes of keys [4v, 4v + 4) of a raw tile (v = 0..7: every
-// wave of the workgroup converts an eighth) into the bf16 buffer (row k at
-// k * kCvtPitch), copies their four block scales into the tile's scale table
-// (scale b of key k at 32 b + k), and zeroes, in the raw tile, the NoPE bytes
-// of those keys at or past `nvalid`: they score -inf and get P = 0, but 0 * NaN
-// would still poison PV if such a record decodes to NaN (the by-index loader
-// reads record 0 for them).  Lane l handles 8-byte units (l & 15) + 16 j, j < 4,
-// of key 4v + (l >> 4): each group of 16 lanes writes 256 contiguous bytes.
-__device__ __forceinline__ void convert_nope_eighth(LDS_AS uint8_t* raw, LDS_AS uint8_t* cvt, LDS_AS float* scales,
-                                                    int v8, int nvalid) {
-  int l = threadIdx.x & 63;
-  asm volatile("" : "+v"(l));  // addresses formed here, not hoisted out of the tile loop (and spilled)
-  const int key = 4 * v8 + (l >> 4);
-  LDS_AS uint8_t* src = raw + key * kRecBytes + 8 * (l & 15);
-  LDS_AS uint8_t* dst = cvt + key * kCvtPitch + 16 * (l & 15);
-  float sc = 0.f;
-  const int skey = 4 * v8 + ((l >> 2) & 3), sb = l & 3;
-  if (l < 16) sc = *reinterpret_cast<const LDS_AS float*>(raw + skey * kRecBytes + 512 + 4 * sb);
-  u32x2 v[4];
+// PV wave w's share of converting raw tile `raw` into bf16 tile `kt` (dense
+// layout, key row k, 16-B chunk c at tile_off(k, c)):
+//   * NoPE block w of all 32 keys: lane l converts the 8 bytes (l & 15) of the
+//     block of keys 4i + (l >> 4), i < 8, into chunk 16w + (l & 15);
+//   * RoPE chunk (l & 7) of key 8w + (l >> 3), copied;
+//   * scale w of key l (l < 32) into the PV table (sp[32w + k]) and the QK
+//     table (sq[4k + w]).
+// Keys at or past nvalid get zeros.  Eight consecutive lanes write one aligned
+// 128-B span of a row (conflict-free 16-B writes).  All reads are issued
+// before the first conversion.
+template <bool FULL>
+__device__ __forceinline__ void convert_block_t(const LDS_AS uint8_t* raw, LDS_AS uint8_t* kt, LDS_AS float* sp,
+                                                LDS_AS float* sq, int w, int nvalid) {
+  const int l = lane_id_here();  // addresses formed here, not hoisted out of the tile loop (and spilled)
+  const int cc = l & 15, kq = l >> 4;
+  u32x2 v[8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<const LDS_AS u32x2*>(src + 128 * j);
+  for (int i = 0; i < 8; ++i)
+    v[i] = *reinterpret_cast<const LDS_AS u32x2*>(raw + (4 * i + kq) * kRecBytes + 128 * w + 8 * cc);
+  const int rk = 8 * w + (l >> 3);
+  const u32x4 rp = *reinterpret_cast<const LDS_AS u32x4*>(raw + rk * kRecBytes + 528 + 16 * (l & 7));
+  float s = 0.f;
+  if (l < 32) s = *reinterpret_cast<const LDS_AS float*>(raw + l * kRecBytes + 512 + 4 * w);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) *reinterpret_cast<LDS_AS bf16x8*>(dst + 256 * j) = e4m3x8_to_bf16(v[j]);
-  if (l < 16) scales[32 * sb + skey] = sc;
-  if (nvalid < kTK && key >= nvalid) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<LDS_AS u32x2*>(src + 128 * j) = u32x2{0u, 0u};
+  for (int i = 0; i < 8; ++i) {
+    const int key = 4 * i + kq;
+    bf16x8 x = e4m3x8_to_bf16(v[i]);
+    if (!FULL && key >= nvalid) x = bf16x8{};
+    *reinterpret_cast<LDS_AS bf16x8*>(kt + tile_off(key, 16 * w + cc)) = x;
   }
+  *reinterpret_cast<LDS_AS u32x4*>(kt + tile_off(rk, 64 + (l & 7))) =
+      (FULL || rk < nvalid) ? rp : u32x4{0u, 0u, 0u, 0u};
+  if (l < 32) {
+    if (!FULL && l >= nvalid) s = 0.f;
+    sp[32 * w + l] = s;
+    sq[4 * l + w] = s;
+  }
+}
+__device__ __forceinline__ void convert_block(const LDS_AS uint8_t* raw, LDS_AS uint8_t* kt, LDS_AS float* sp,
+                                              LDS_AS float* sq, int w, int nvalid) {
+  if (nvalid >= kTK) convert_block_t<true>(raw, kt, sp, sq, w, nvalid);
+  else convert_block_t<false>(raw, kt, sp, sq, w, nvalid);
 }
 
 template <bool IDX>
@@ -1234,8 +1255,8 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
   using Loader = std::conditional_t<IDX, IndexedLoader, TileLoader<true>>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[IDX ? kF8LdsBytesIdx : kF8LdsBytes];
   LDS_AS uint8_t* smem = (LDS_AS uint8_t*)(smem_raw);
-  LDS_AS uint8_t* cvt = smem + kF8OffC;
-  LDS_AS float* scales_s = reinterpret_cast<LDS_AS float*>(smem + kF8OffS);     // [4 tiles][4 blocks][32 keys]
+  LDS_AS float* sp_s = reinterpret_cast<LDS_AS float*>(smem + kF8OffS);        // [4 tiles][4 blocks][32 keys]
+  LDS_AS float* sq_s = reinterpret_cast<LDS_AS float*>(smem + kF8OffSq);       // [2 tiles][32 keys][4 blocks]
   LDS_AS float* alpha_s = reinterpret_cast<LDS_AS float*>(smem + kF8OffAlpha);  // [2][64]
   LDS_AS uint8_t* flag_s = smem + kF8OffFlag;                                    // [2][4] bytes
   LDS_AS float* l_s = reinterpret_cast<LDS_AS float*>(smem + kF8OffL);
@@ -1259,8 +1280,8 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
 
   Loader loader;
   loader.init(w, l);  // used by the QK waves
-  // loads of the tile in flight that a QK wave may leave outstanding while it
-  // waits for the next one (wave-uniform)
+  // loads of the newest tile in flight that a QK wave may leave outstanding
+  // while it waits for the one before (wave-uniform)
   const bool wave0 = w == 0;
   auto wait_all_but_inflight = [&]() {
     if constexpr (IDX) {
@@ -1271,9 +1292,16 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
     }
   };
   const int row_local = 16 * w + li;
-  // PV: lane j of 16-lane group g addresses key 8g + j/2, column half j & 1
-  const int tr8_key = 8 * g + (li >> 1);
-  const int tr8_col = 8 * (li & 1);
+  // the dense kernel's operand reads of a bf16 tile: QK^T (K as the A operand)
+  // and the transposed V reads, odd lane groups reading their upper 4-key half
+  // first (P^T is built in the same key order)
+  const int kx = li & 7;
+  const uint32_t kq_base0 = (uint32_t)(li * kRowBytes + 16 * (4 * (0 ^ (kx >> 2)) + (g ^ (kx & 3))));
+  const uint32_t kq_base1 = (uint32_t)(li * kRowBytes + 16 * (4 * (1 ^ (kx >> 2)) + (g ^ (kx & 3))));
+  const int kh0 = 8 * g + 4 * (g & 1), kh1 = 8 * g + 4 * ((g & 1) ^ 1);  // keys of the two halves
+  const int kr0 = kh0 + (li >> 2), kr1 = kh1 + (li >> 2);
+  const int tr_j = li & 3;
+  const uint32_t tr_within = (tr_j & 1) * 8;
 
   for (int r = begin_req; r <= end_req; ++r) {
     int seqlen = ld_const(a.seqlens, r);
@@ -1298,8 +1326,9 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
       if (threadIdx.x == 0) atomicOr(&g_error_flags, kErrMeta);
       continue;
     }
-    const int rho = rbk * MB + row_local;
-    auto raw_slot = [&](int t) -> LDS_AS uint8_t* { return smem + kOffRaw + (t & 3) * kRawTileBytes; };
+    auto raw_slot = [&](int t) -> LDS_AS uint8_t* { return smem + kOffRaw + (t % kF8RawSlots) * kRawTileBytes; };
+    auto bf_tile = [&](int t) -> LDS_AS uint8_t* { return smem + (t & 1) * kTileBytes; };
+    auto nvalid_of = [&](int t) { return min(kTK, t1 - (t0 + t * kTK)); };
     if constexpr (IDX) {
       // the piece's first kIdxCache top-k ids -> LDS, read by the ring loads
       // (later ids, if any, are read directly)
@@ -1313,10 +1342,14 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
 
     if (is_qk) {
       // ================================================================ QK waves
-      const bool live = rho < a.M;
+      bool live;
       bf16x8 qreg[18];
       {
-        const uint16_t* qrow = a.q + ((int64_t)r * a.M + (live ? rho : 0)) * kDQK + 8 * g;
+        // the Q address is formed here, not hoisted out of the request loop (and spilled)
+        const int ln = lane_id_here();
+        const int rq = rbk * MB + 16 * w + (ln & 15);
+        live = rq < a.M;
+        const uint16_t* qrow = a.q + ((int64_t)r * a.M + (live ? rq : 0)) * kDQK + 8 * (ln >> 4);
 #pragma unroll
         for (int s = 0; s < 18; ++s) {
           const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 32 * s);
@@ -1381,18 +1414,15 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
         }
       };
 
-      // QK^T of tile t: NoPE k-steps (s < 16) from the converted buffer (key
-      // 16 kb + li at kb * 16 * kCvtPitch + li * kCvtPitch, dims 32 s + 8 g ..),
-      // RoPE k-steps from the raw records; scores combined with the block scales
-      // -> sx
+      // QK^T of tile t from bf16 tile t & 1: NoPE k-steps (s < 16) into block
+      // s / 4, RoPE k-steps into their own sum; scores combined with the block
+      // scales of the QK table -> sx
       auto qk = [&](int t, auto hook) {
-        const LDS_AS uint8_t* rawt = raw_slot(t);
-        const LDS_AS uint8_t* c0 = cvt + li * kCvtPitch + 16 * g;
-        const LDS_AS uint8_t* c1 = c0 + 16 * kCvtPitch;
-        const LDS_AS uint8_t* r0 = rawt + li * kRecBytes + 528 + 16 * g;
-        const LDS_AS uint8_t* r1 = r0 + 16 * kRecBytes;
-        auto rd0 = [&](int s) { return lds_read_b128(s < 16 ? c0 + 64 * s : r0 + 64 * (s - 16)); };
-        auto rd1 = [&](int s) { return lds_read_b128(s < 16 ? c1 + 64 * s : r1 + 64 * (s - 16)); };
+        const LDS_AS uint8_t* kt = bf_tile(t);
+        const LDS_AS float* sq = sq_s + (t & 1) * kTK * 4;
+        auto addr = [&](int s) { return ((s & 1) ? kq_base1 : kq_base0) + (uint32_t)((s >> 1) * 128); };
+        auto rd0 = [&](int s) { return lds_read_b128(kt + addr(s)); };
+        auto rd1 = [&](int s) { return lds_read_b128(kt + addr(s) + 16 * kRowBytes); };
         constexpr int D = kQkDepth;
         f32x4 acc[2][5];
 #pragma unroll
@@ -1417,16 +1447,13 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
           hook(s);
           __builtin_amdgcn_sched_barrier(0);
         }
-        // scores: RoPE part + sum over NoPE blocks of scale_b * block sum, masked
         const int key0 = t0 + t * kTK;
-        const int nvalid = min(kTK, t1 - key0);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int kr = 16 * kb + 4 * g + i;
-            const f32x4 sc = kr < nvalid ? *reinterpret_cast<const LDS_AS f32x4*>(rawt + kr * kRecBytes + 512)
-                                         : f32x4{0.f, 0.f, 0.f, 0.f};
+            const f32x4 sc = *reinterpret_cast<const LDS_AS f32x4*>(sq + 4 * kr);  // 0 past the valid count
             float x = acc[kb][4][i] + sc[0] * acc[kb][0][i] + sc[1] * acc[kb][1][i] + sc[2] * acc[kb][2][i] +
                       sc[3] * acc[kb][3][i];
             x *= a.scale_log2;
@@ -1434,19 +1461,20 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
           }
       };
 
+      // the ring: raw tiles 0..2 now; tiles 0 and 1 resident before the PV
+      // waves convert tile 0 (and, in iteration 0, tile 1)
       if (ntile > 0) loader.issue(a, lrow, t0, smem, 0, w);
       if (ntile > 1) loader.issue(a, lrow, t0 + kTK, smem, 1, w);
-      if (ntile > 1) wait_all_but_inflight();
+      if (ntile > 2) loader.issue(a, lrow, t0 + 2 * kTK, smem, 2, w);
+      if (ntile > 2) wait_all_but_inflight();
       else wait_vmcnt<0>();
-      sync_lds();  // tile 0 resident
+      sync_lds();  // raw tiles 0 and 1 resident
+      sync_lds();  // bf16 tile 0 converted
       auto iter = [&](auto do_qk_c, auto do_sm_c, int t) {
         constexpr bool DO_QK = decltype(do_qk_c)::value;
         constexpr bool DO_SM = decltype(do_sm_c)::value;
-        const bool more = t + 2 < ntile;
-        if (more) loader.issue(a, lrow, t0 + (t + 2) * kTK, smem, (t + 2) & 3, w);
-        if (t < ntile)
-          convert_nope_eighth(raw_slot(t), cvt, scales_s + (t & 3) * 4 * kTK, w, min(kTK, t1 - (t0 + t * kTK)));
-        sync_lds();  // tile t's NoPE K converted (by all eight waves)
+        const bool more = t + 3 < ntile;
+        if (more) loader.issue(a, lrow, t0 + (t + 3) * kTK, smem, t % kF8RawSlots, w);
         if constexpr (DO_QK) {
           if constexpr (DO_SM) {
             // the softmax of t-1 reads sx, which qk(t) overwrites only at its end
@@ -1460,21 +1488,21 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
         }
         if (t == ntile) {  // every tile's softmax is done: row sums for the output stage
           const float lt = row4_sum(lpart);
-          if (g == 0) {
-            l_s[row_local] = lt;
-            if (rho < a.M) {
+          // the row index is formed here: otherwise the compiler hoists the LDS
+          // and 64-bit store addresses out of the request loop and spills them
+          const int ln = lane_id_here();
+          if (ln < 16) {
+            const int rl = 16 * w + ln;
+            l_s[rl] = lt;
+            const int gr = rbk * MB + rl;
+            if (gr < a.M) {
               const float lse = lt > 0.f ? (mrow + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
-              // by index, the row index is made opaque: otherwise the compiler
-              // hoists the 64-bit store addresses out of the request loop and
-              // spills them
-              int gr = rho;
-              if constexpr (IDX) asm volatile("" : "+v"(gr));
               if (nsplit == 1) a.lse[(int64_t)r * a.M + gr] = lse;
               else a.part_lse[(int64_t)slot * a.M + gr] = lse;
             }
           }
         }
-        if (t + 1 < ntile) {
+        if (t + 2 < ntile) {  // raw tile t+2 resident before the barrier (converted next iteration)
           if (more) wait_all_but_inflight();
           else wait_vmcnt<0>();
         }
@@ -1497,37 +1525,48 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
       for (int db = 0; db < 8; ++db)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      u32x2 v[8];  // raw V^T fragments of one tile (this wave's 128 columns, 32 keys)
+      bf16x8 v8[8];  // V^T fragments of one tile (this wave's 128 columns, 32 keys)
+      uint32_t voff0[4], voff1[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int c = 16 * w + 2 * d + (tr_j >> 1);
+        voff0[d] = tile_off(kr0, c) + tr_within;
+        voff1[d] = tile_off(kr1, c) + tr_within;
+      }
       auto vread = [&](int t, int db) {
-        v[db] = lds_read_tr8(raw_slot(t) + tr8_key * kRecBytes + 128 * w + 16 * db + tr8_col);
+        const LDS_AS uint8_t* kt = bf_tile(t) + (db >> 2) * 128;
+        v8[db] = __builtin_shufflevector(lds_read_tr16(kt + voff0[db & 3]), lds_read_tr16(kt + voff1[db & 3]), 0, 1, 2, 3,
+                                         4, 5, 6, 7);
       };
-      sync_lds();  // tile 0 resident
-      // one iteration: PV(t-2) from registers, V(t-1) into registers; the
-      // conversion barrier of the QK waves falls after the first four 16-column
-      // blocks
+      auto convert = [&](int t) {
+        convert_block(raw_slot(t), bf_tile(t), sp_s + (t & 3) * 4 * kTK, sq_s + (t & 1) * kTK * 4, w, nvalid_of(t));
+      };
+      sync_lds();  // raw tiles 0 and 1 resident
+      if (ntile > 0) convert(0);
+      sync_lds();  // bf16 tile 0 converted
+      // one iteration: PV(t-2) from registers, V(t-1) into registers, then raw
+      // tile t+1 converted into the bf16 tile V(t-1) came from
       auto iter = [&](auto do_pv_c, auto do_vread_c, int t) {
         constexpr bool DO_PV = decltype(do_pv_c)::value;
         constexpr bool DO_VREAD = decltype(do_vread_c)::value;
         const int tp = t - 2;
-        if (t < ntile)
-          convert_nope_eighth(raw_slot(t), cvt, scales_s + (t & 3) * 4 * kTK, 4 + w, min(kTK, t1 - (t0 + t * kTK)));
-        sync_lds();  // the conversion barrier
         uint32_t fl = 0;
         float al[RB];
         bf16x8 bp[RB];
         if constexpr (DO_PV) {
-          // P^T operand of row 16 rb + li: keys 8g .. 8g+7 of P(t-2) times their scale w
-          const LDS_AS uint8_t* pb = smem + kF8OffP + (tp & 1) * kF8PBuf + li * kF8PPitch + 32 * g;
-          const LDS_AS float* sp = scales_s + (tp & 3) * 4 * kTK + kTK * w + 8 * g;
-          const f32x4 s0 = *reinterpret_cast<const LDS_AS f32x4*>(sp);
-          const f32x4 s1 = *reinterpret_cast<const LDS_AS f32x4*>(sp + 4);
+          // P^T operand of row 16 rb + li: the two 4-key halves of keys 8g..8g+7
+          // of P(t-2), in the order of the V^T reads, times their scale w
+          const LDS_AS uint8_t* pb = smem + kF8OffP + (tp & 1) * kF8PBuf + li * kF8PPitch;
+          const LDS_AS float* sp = sp_s + (tp & 3) * 4 * kTK + kTK * w;
+          const f32x4 s0 = *reinterpret_cast<const LDS_AS f32x4*>(sp + kh0);
+          const f32x4 s1 = *reinterpret_cast<const LDS_AS f32x4*>(sp + kh1);
           fl = *reinterpret_cast<const LDS_AS uint32_t*>(flag_s + (tp & 1) * 4);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) al[rb] = alpha_s[(tp & 1) * kMaxRowsPerWG + 16 * rb + li];
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) {
-            const f32x4 p0 = *reinterpret_cast<const LDS_AS f32x4*>(pb + 16 * rb * kF8PPitch);
-            const f32x4 p1 = *reinterpret_cast<const LDS_AS f32x4*>(pb + 16 * rb * kF8PPitch + 16);
+            const f32x4 p0 = *reinterpret_cast<const LDS_AS f32x4*>(pb + 16 * rb * kF8PPitch + 4 * kh0);
+            const f32x4 p1 = *reinterpret_cast<const LDS_AS f32x4*>(pb + 16 * rb * kF8PPitch + 4 * kh1);
             bp[rb] = __builtin_bit_cast(
                 bf16x8, u32x4{pack_bf16x2(p0[0] * s0[0], p0[1] * s0[1]), pack_bf16x2(p0[2] * s0[2], p0[3] * s0[3]),
                               pack_bf16x2(p1[0] * s1[0], p1[1] * s1[1]), pack_bf16x2(p1[2] * s1[2], p1[3] * s1[3])});
@@ -1547,9 +1586,8 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
 #pragma unroll
           for (int db = db0; db < db0 + 4; ++db) {
             if constexpr (DO_PV) {
-              const bf16x8 av = e4m3x8_to_bf16(v[db]);
 #pragma unroll
-              for (int rb = 0; rb < RB; ++rb) o[db][rb] = mfma16(av, bp[rb], o[db][rb]);
+              for (int rb = 0; rb < RB; ++rb) o[db][rb] = mfma16(v8[db], bp[rb], o[db][rb]);
             }
             if constexpr (DO_VREAD) vread(t - 1, db);
             __builtin_amdgcn_sched_barrier(0);
@@ -1557,6 +1595,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
         };
         blocks(0);
         blocks(4);
+        if (t + 1 < ntile) convert(t + 1);
         sync_lds();
       };
       using F = std::false_type;
@@ -1570,22 +1609,25 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
         iter(F{}, F{}, 1);
       }
       sync_lds();  // l from the QK waves (written in iteration ntile)
+      // output rows and addresses formed here from opaque lane indices: the
+      // compiler otherwise hoists them out of the request loop and spills them
+      int col = 128 * w + 4 * g, lo = li;
+      asm volatile("" : "+v"(col), "+v"(lo));
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        int rho_o = rbk * MB + 16 * rb + li;
+        const int rho_o = rbk * MB + 16 * rb + lo;
         if (rho_o >= a.M) continue;
-        if constexpr (IDX) asm volatile("" : "+v"(rho_o));  // keeps the row addresses from being hoisted and spilled
         const float lt = l_s[16 * rb + li];
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         if (nsplit == 1) {
-          uint16_t* orow = a.out + ((int64_t)r * a.M + rho_o) * kDV + 128 * w + 4 * g;
+          uint16_t* orow = a.out + ((int64_t)r * a.M + rho_o) * kDV + col;
 #pragma unroll
           for (int db = 0; db < 8; ++db) {
             const f32x4 vv = o[db][rb] * inv;
             *reinterpret_cast<u32x2*>(orow + 16 * db) = u32x2{pack_bf16x2(vv[0], vv[1]), pack_bf16x2(vv[2], vv[3])};
           }
         } else {
-          float* prow = a.part_o + ((int64_t)slot * a.M + rho_o) * kDV + 128 * w + 4 * g;
+          float* prow = a.part_o + ((int64_t)slot * a.M + rho_o) * kDV + col;
 #pragma unroll
           for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(prow + 16 * db) = o[db][rb] * inv;
         }

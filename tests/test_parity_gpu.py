@@ -463,8 +463,9 @@ SPARSE = [
     ("topk2048-h128", 152, 2, 128, 2048, [2048, 2048], 32768, None),
     ("tails-h128", 153, 3, 128, 512, [400, 17, 512], 8192, 7),
     ("empty-h64", 154, 2, 64, 128, [0, 77], 1024, None),
-    # pieces longer than the 2048 top-k ids the by-index decode stages per piece: the
+    # pieces longer than the 1024 top-k ids the by-index decode stages per piece: the
     # later tiles read their ids directly
+    ("topk1500-h128-p1", 168, 1, 128, 2048, [1500], 8192, 1),
     ("topk3000-h64-p1", 155, 1, 64, 4096, [3000], 16384, 1),
     ("topk4096-h128-p3", 156, 2, 128, 4096, [4096, 2500], 32768, 3),
 ]
