@@ -1220,20 +1220,23 @@ __device__ __forceinline__ void convert_block_t(const LDS_AS uint8_t* raw, LDS_A
                                                 LDS_AS float* sq, int w, int nvalid) {
   const int l = lane_id_here();  // addresses formed here, not hoisted out of the tile loop (and spilled)
   const int cc = l & 15, kq = l >> 4;
+  // key 4i + kq: its raw bytes at src + 4i records, its bf16 chunk at d0 (i even)
+  // or d1 (i odd) + (i / 2) * 8 rows (the swizzle depends on the key mod 8 only)
+  const LDS_AS uint8_t* src = raw + kq * kRecBytes + 128 * w + 8 * cc;
+  LDS_AS uint8_t* const d0 = kt + tile_off(kq, 16 * w + cc);
+  LDS_AS uint8_t* const d1 = kt + tile_off(4 + kq, 16 * w + cc);
   u32x2 v[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    v[i] = *reinterpret_cast<const LDS_AS u32x2*>(raw + (4 * i + kq) * kRecBytes + 128 * w + 8 * cc);
+  for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const LDS_AS u32x2*>(src + 4 * i * kRecBytes);
   const int rk = 8 * w + (l >> 3);
   const u32x4 rp = *reinterpret_cast<const LDS_AS u32x4*>(raw + rk * kRecBytes + 528 + 16 * (l & 7));
   float s = 0.f;
   if (l < 32) s = *reinterpret_cast<const LDS_AS float*>(raw + l * kRecBytes + 512 + 4 * w);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int key = 4 * i + kq;
     bf16x8 x = e4m3x8_to_bf16(v[i]);
-    if (!FULL && key >= nvalid) x = bf16x8{};
-    *reinterpret_cast<LDS_AS bf16x8*>(kt + tile_off(key, 16 * w + cc)) = x;
+    if (!FULL && 4 * i + kq >= nvalid) x = bf16x8{};
+    *reinterpret_cast<LDS_AS bf16x8*>(((i & 1) ? d1 : d0) + (i >> 1) * 8 * kRowBytes) = x;
   }
   *reinterpret_cast<LDS_AS u32x4*>(kt + tile_off(rk, 64 + (l & 7))) =
       (FULL || rk < nvalid) ? rp : u32x4{0u, 0u, 0u, 0u};
@@ -1357,6 +1360,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
         }
       }
       const int lim = live ? t1 : 0;
+      const int lim_min = __all(live) ? t1 : 0;  // every row of the wave sees keys below this
       float mrow = -INFINITY, lpart = 0.f;
       float sx[8];  // scaled scores of the tile whose softmax runs next (keys 16kb + 4g + i)
 #pragma unroll
@@ -1457,8 +1461,15 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
             float x = acc[kb][4][i] + sc[0] * acc[kb][0][i] + sc[1] * acc[kb][1][i] + sc[2] * acc[kb][2][i] +
                       sc[3] * acc[kb][3][i];
             x *= a.scale_log2;
-            sx[kb * 4 + i] = key0 + kr < lim ? x : -INFINITY;
+            sx[kb * 4 + i] = x;
           }
+        if (key0 + kTK > lim_min) {  // wave-uniform: some row of the wave does not see the whole tile
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (key0 + 16 * kb + 4 * g + i >= lim) sx[kb * 4 + i] = -INFINITY;
+        }
       };
 
       // the ring: raw tiles 0..2 now; tiles 0 and 1 resident before the PV
