@@ -1561,51 +1561,41 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
         constexpr bool DO_PV = decltype(do_pv_c)::value;
         constexpr bool DO_VREAD = decltype(do_vread_c)::value;
         const int tp = t - 2;
-        uint32_t fl = 0;
-        float al[RB];
-        bf16x8 bp[RB];
         if constexpr (DO_PV) {
           // P^T operand of row 16 rb + li: the two 4-key halves of keys 8g..8g+7
-          // of P(t-2), in the order of the V^T reads, times their scale w
+          // of P(t-2), in the order of the V^T reads, times their scale w.  One
+          // row block at a time: forming the operand of row block rb + 1 runs
+          // while the MFMAs of row block rb are in the pipe.
           const LDS_AS uint8_t* pb = smem + kF8OffP + (tp & 1) * kF8PBuf + li * kF8PPitch;
           const LDS_AS float* sp = sp_s + (tp & 3) * 4 * kTK + kTK * w;
           const f32x4 s0 = *reinterpret_cast<const LDS_AS f32x4*>(sp + kh0);
           const f32x4 s1 = *reinterpret_cast<const LDS_AS f32x4*>(sp + kh1);
-          fl = *reinterpret_cast<const LDS_AS uint32_t*>(flag_s + (tp & 1) * 4);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) al[rb] = alpha_s[(tp & 1) * kMaxRowsPerWG + 16 * rb + li];
+          const uint32_t fls =
+              tp > 0 ? __builtin_amdgcn_readfirstlane(*reinterpret_cast<const LDS_AS uint32_t*>(flag_s + (tp & 1) * 4))
+                     : 0u;
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) {
             const f32x4 p0 = *reinterpret_cast<const LDS_AS f32x4*>(pb + 16 * rb * kF8PPitch + 4 * kh0);
             const f32x4 p1 = *reinterpret_cast<const LDS_AS f32x4*>(pb + 16 * rb * kF8PPitch + 4 * kh1);
-            bp[rb] = __builtin_bit_cast(
+            const bf16x8 bq = __builtin_bit_cast(
                 bf16x8, u32x4{pack_bf16x2(p0[0] * s0[0], p0[1] * s0[1]), pack_bf16x2(p0[2] * s0[2], p0[3] * s0[3]),
                               pack_bf16x2(p1[0] * s1[0], p1[1] * s1[1]), pack_bf16x2(p1[2] * s1[2], p1[3] * s1[3])});
-          }
-          if (tp > 0) {
-            const uint32_t fls = __builtin_amdgcn_readfirstlane(fl);
+            if ((fls >> (8 * rb)) & 0xffu) {  // the running max of this row block moved
+              const float al = alpha_s[(tp & 1) * kMaxRowsPerWG + 16 * rb + li];
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-              if ((fls >> (8 * rb)) & 0xffu) {
-#pragma unroll
-                for (int db = 0; db < 8; ++db) o[db][rb] *= al[rb];
-              }
+              for (int db = 0; db < 8; ++db) o[db][rb] *= al;
             }
-          }
-        }
-        auto blocks = [&](int db0) {
 #pragma unroll
-          for (int db = db0; db < db0 + 4; ++db) {
-            if constexpr (DO_PV) {
-#pragma unroll
-              for (int rb = 0; rb < RB; ++rb) o[db][rb] = mfma16(v8[db], bp[rb], o[db][rb]);
-            }
-            if constexpr (DO_VREAD) vread(t - 1, db);
+            for (int db = 0; db < 8; ++db) o[db][rb] = mfma16(v8[db], bq, o[db][rb]);
             __builtin_amdgcn_sched_barrier(0);
           }
-        };
-        blocks(0);
-        blocks(4);
+        }
+        // V(t-1) into the registers PV(t-2) has finished with; then raw tile t+1
+        // converted into the bf16 tile those reads came from
+        if constexpr (DO_VREAD) {
+#pragma unroll
+          for (int db = 0; db < 8; ++db) vread(t - 1, db);
+        }
         if (t + 1 < ntile) convert(t + 1);
         sync_lds();
       };
