@@ -60,8 +60,10 @@ int hip_fail(hipError_t e, const char* what) {
 // b = 1 takes 21.7 / 27.6 / 36.6 / 60.5 us at sk = 1024 / 4096 / 16384 / 65536
 // with 16 / 16 / 64 / 64 pieces, against 47.8 and 129.0 us for the last two at
 // 16; b = 4, sk = 4096 is fastest at 64 (32.0 us against 33.5 at 128).  The
-// FP8 kernel is slower per tile and gains from finer pieces (C5: 45.9 us at 16
-// per request, 38.7 us at 32, 38.5 us at 64).
+// FP8 kernel is slower per tile and gains from finer pieces (C5, packed decode
+// + combine, cold: 35.8 us at 16 per request, 29.8 at 24, 28.8 at 32, 29.0 at
+// 48 and 64; b = 64, h_q = 128, top-k 2048 is fastest at the plan's 2 per
+// request: 80.4 us against 92.9 at 4).
 constexpr int kMaxSplitsPerRequest = mla::kSplitCeilPerRequest;
 constexpr int kMaxSplitsPerRequestFp8 = 32;
 
