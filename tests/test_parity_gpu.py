@@ -468,6 +468,11 @@ SPARSE = [
     ("topk1500-h128-p1", 168, 1, 128, 2048, [1500], 8192, 1),
     ("topk3000-h64-p1", 155, 1, 64, 4096, [3000], 16384, 1),
     ("topk4096-h128-p3", 156, 2, 128, 4096, [4096, 2500], 32768, 3),
+    # the tile pipeline's edges: pieces of 1..4 tiles (the first tile converted
+    # before the loop, the rest one iteration ahead) ending at every kind of
+    # tail, several requests per workgroup (LDS reused from one to the next)
+    ("pipeline-edges-h64-p3", 169, 12, 64, 128, [1, 31, 32, 33, 63, 64, 65, 95, 96, 97, 127, 128], 4096, 3),
+    ("pipeline-edges-h128", 170, 12, 128, 128, [1, 31, 32, 33, 63, 64, 65, 95, 96, 97, 127, 128], 4096, None),
 ]
 
 
