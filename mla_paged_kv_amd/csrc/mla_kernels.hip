@@ -202,6 +202,14 @@ __device__ __forceinline__ uint32_t tile_off(int kr, int c) {
   return (uint32_t)(kr * kRowBytes + ((c ^ (kr & 7)) << 4));
 }
 
+// Scheduler part of workgroup column b of a decode grid with P columns.  The
+// dispatcher hands workgroups to the 8 XCDs round-robin by linear id (x + P y),
+// so with P a multiple of 8 column b runs on XCD b mod 8 for every row block
+// y; mapping b to part (b mod 8) * P/8 + b/8 gives each XCD a contiguous range
+// of parts, and the pieces of one request (consecutive parts), which read the
+// same Q rows, share an L2.
+__device__ __forceinline__ int xcd_part(int b, int P) { return (P & 7) ? b : (b & 7) * (P >> 3) + (b >> 3); }
+
 // Lane id in [0, 64), computed where it is used: the asm is never hoisted, so
 // values derived from it do not stay live (and spill) across the tile loops.
 // Every lane of the wave must be active.
@@ -756,7 +764,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
   const int w = wv & 3;  // index within the role
   const int l = tid & 63, g = l >> 4, li = l & 15;
   const bool has_rows = is_qk && w < RB;
-  const int part = blockIdx.x;
+  const int part = xcd_part(blockIdx.x, gridDim.x);
   // several KV heads: grid.y = h_kv * row blocks per head; the Mkv = s_q * G
   // rows of KV head kvh (G = h_q / h_kv query heads each) are numbered
   // s * G + hh, and are row s * h_q + kvh * G + hh of the request
@@ -1269,7 +1277,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
   const bool is_qk = wv < 4;
   const int w = wv & 3;
   const int l = tid & 63, g = l >> 4, li = l & 15;
-  const int part = blockIdx.x, rbk = blockIdx.y;
+  const int part = xcd_part(blockIdx.x, gridDim.x), rbk = blockIdx.y;
   const int begin_req = ld_const(a.sched_meta, part * 8 + 0);
   if (begin_req < 0) return;
   const int begin_blk = ld_const(a.sched_meta, part * 8 + 1);
