@@ -24,9 +24,12 @@
 //   * Online softmax in the exp2 domain with lazy rescaling: the running max
 //     moves (and O is rescaled) only when a tile's max exceeds it by more than
 //     kRescaleThreshold (log2 units); final out = O / l is exact either way.
-//   * The FP8 paths keep the raw 656-byte records in the ring and convert the
-//     E4M3 bytes to bf16 in registers on their way to the MFMAs (exact); each
-//     key's fp32 block scales multiply the per-block score sums and P.
+//   * The FP8 paths stream the raw 656-byte records into a ring of their own;
+//     the PV waves convert each tile's E4M3 bytes to bf16 (exact) into a tile
+//     in the dense layout one iteration before it is used, and each key's fp32
+//     block scales multiply the per-block score sums and P.
+//   * A launch's parts are mapped so that each XCD runs a contiguous range of
+//     them (the pieces of a request share an L2).
 #include "mla_internal.h"
 
 #include <mutex>
