@@ -822,7 +822,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
     }
     const int nblk = (seqlen + kPage - 1) / kPage;
     const int blk0 = (r == begin_req) ? begin_blk : 0;
-    const int blk1 = (r == end_req) ? end_blk : nblk;
+    const int blk1 = min((r == end_req) ? end_blk : nblk, nblk);
     const int t0 = blk0 * kPage;
     const int t1 = min(blk1 * kPage, seqlen);
     const int ntile = t1 > t0 ? (t1 - t0 + kTK - 1) / kTK : 0;
@@ -835,19 +835,22 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
       continue;
     }
     const int rho = rbk * MB + row_local;
-    // page ids of this piece's first kPageCache blocks -> LDS (the tile loop then
-    // never waits on a scalar load); later blocks, if any, are looked up directly
+    auto uniform = [](int raw) -> int64_t { return __builtin_amdgcn_readfirstlane(raw); };
+    // The PV waves start the ring at once: tiles 0 and 1 lie in the piece's
+    // first page (t0 is page-aligned), whose id is one scalar load.  Meanwhile
+    // the QK waves load Q and copy the page ids of the piece's first
+    // kPageCache blocks to LDS (the tile loop then never waits on a scalar
+    // load; later blocks, if any, are looked up directly).  Only the QK waves
+    // touch the page ids with vector loads: in a PV wave the wait for them
+    // would also wait for the tiles already in flight (vmcnt retires in order).
     const int ncache = min(blk1 - blk0, kPageCache);
-    for (int i = tid; i < ncache; i += kWsThreads)
-      pages_s[i] = a.block_table[(int64_t)r * a.max_pages + blk0 + i];
-    sync_lds();
-    // page id of tile t: an LDS read (or, past the cached range, a scalar load)
-    // that is made wave-uniform only where it is used
+    // page id of tile t (valid after the barrier below): an LDS read (or, past
+    // the cached range, a scalar load) that is made wave-uniform only where it
+    // is used
     auto page_raw = [&](int t) -> int {
       const int b = (t0 + t * kTK) / kPage - blk0;
       return b < kPageCache ? pages_s[b] : ld_const(a.block_table, (int64_t)r * a.max_pages + blk0 + b);
     };
-    auto uniform = [](int raw) -> int64_t { return __builtin_amdgcn_readfirstlane(raw); };
 
     if (is_qk) {
       // ================================================================ QK waves
@@ -860,7 +863,14 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
           const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 32 * s);
           qreg[s] = live ? v : bf16x8{};
         }
+        static_assert(kPageCache == 2 * 256, "two page ids per QK-wave thread");
+        const int32_t* bt = a.block_table + (int64_t)r * a.max_pages + blk0;
+        const int pa = tid < ncache ? bt[tid] : 0;
+        const int pb = tid + 256 < ncache ? bt[tid + 256] : 0;
+        if (tid < ncache) pages_s[tid] = pa;
+        if (tid + 256 < ncache) pages_s[tid + 256] = pb;
       }
+      sync_lds();  // page ids in LDS (the PV waves' matching barrier follows their first loads)
       int lim = 0;
       if (live) {
         int nvis = seqlen;
@@ -1052,8 +1062,12 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
       };
 
       // The ring: tiles 0 and 1 now, tile t+2 at the start of iteration t.
-      if (ntile > 0) issue_tile(uniform(page_raw(0)), t0, 0);
-      if (ntile > 1) issue_tile(uniform(page_raw(1)), t0 + kTK, 1);
+      if (ntile > 0) {
+        const int64_t p0 = uniform(ld_const(a.block_table, (int64_t)r * a.max_pages + blk0));
+        issue_tile(p0, t0, 0);
+        if (ntile > 1) issue_tile(p0, t0 + kTK, 1);
+      }
+      sync_lds();  // page ids in LDS (filled by the QK waves)
       // page id of the tile the next iteration loads: read before the barrier that
       // ends an iteration (which waits for it) and made wave-uniform after it
       int pg_next = ntile > 2 ? page_raw(2) : 0;
