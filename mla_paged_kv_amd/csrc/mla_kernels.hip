@@ -786,7 +786,8 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_ws_kernel(DecodeArgs a) 
   const int end_req = ld_const(a.sched_meta, part * 8 + 2);
   const int end_blk = ld_const(a.sched_meta, part * 8 + 3);
   const int begin_split = ld_const(a.sched_meta, part * 8 + 4);
-  if (begin_req >= a.batch || end_req >= a.batch || end_req < begin_req) {  // not a scheduler record
+  if (begin_req >= a.batch || end_req >= a.batch || end_req < begin_req || begin_blk < 0 || end_blk < 0) {
+    // not a scheduler record
     if (threadIdx.x == 0) atomicOr(&g_error_flags, kErrMeta);
     return;
   }
@@ -1301,7 +1302,8 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_fp8ws_kernel(DecodeArgs 
   const int end_req = ld_const(a.sched_meta, part * 8 + 2);
   const int end_blk = ld_const(a.sched_meta, part * 8 + 3);
   const int begin_split = ld_const(a.sched_meta, part * 8 + 4);
-  if (begin_req >= a.batch || end_req >= a.batch || end_req < begin_req) {  // not a scheduler record
+  if (begin_req >= a.batch || end_req >= a.batch || end_req < begin_req || begin_blk < 0 || end_blk < 0) {
+    // not a scheduler record
     if (threadIdx.x == 0) atomicOr(&g_error_flags, kErrMeta);
     return;
   }

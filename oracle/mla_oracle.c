@@ -419,13 +419,13 @@ int oracle_mla_sparse_decode(const uint16_t* q, const uint8_t* kcache_rec, int64
                              double* out, double* lse, int nthreads) {
   if (!q || !kcache_rec || !indices || !topk_length || !out || !lse) return OR_BAD_ARG;
   if (batch < 0 || s_q < 1 || h_q < 1 || cap < 0 || num_pages < 0) return OR_BAD_ARG;
-  sparse_ctx c = {{1, NULL, kcache_rec, num_pages}, q, indices, topk_length, batch, s_q, h_q, cap, scale, out, lse};
+  sparse_ctx c = {{1, NULL, kcache_rec, num_pages, 0, 0}, q, indices, topk_length, batch, s_q, h_q, cap, scale, out, lse};
   return run_rows(sparse_row, &c, (int64_t)batch * s_q * h_q, cap, nthreads);
 }
 
 /* Dequantise the record at physical token id `phys` into k[0:576] (for tests). */
 int oracle_decode_record(const uint8_t* kcache_rec, int64_t num_pages, int64_t phys, double* k) {
-  kv_pool p = {1, NULL, kcache_rec, num_pages};
+  kv_pool p = {1, NULL, kcache_rec, num_pages, 0, 0};
   return load_key(&p, phys, k);
 }
 

@@ -722,6 +722,33 @@ def test_topk_length_above_capacity_sets_flag_without_fault():
     assert ops.mla_read_device_errors() & 4
 
 
+def test_corrupt_metadata_sets_flag_without_fault():
+    """A scheduler record that no scheduler produces (a negative block index) is
+    refused by every decode kernel: it sets device flag bit 3 and skips the
+    record, reading nothing through it."""
+    G.say("device flag: corrupt scheduler records (dense, packed, by index)")
+    ops.mla_read_device_errors()  # clear
+    w = W.dense_workload("badmeta", 161, 2, 1, 128, [300, 200], pool_pages=12, num_parts=4)
+    t = G.dev_tensors(w)
+    plan = ops.DecodePlan(t["seqlens"], w.s_q, w.h_q, ops.KV_BF16_PAGED, num_parts=4)
+    assert int(plan.sched_meta[0, 0]) == 0  # part 0 owns blocks (the record is live)
+    plan.sched_meta[0, 1] = -3  # begin block
+    ops.mla_decode(t["q"], t["kcache"], t["block_table"], t["seqlens"], w.scale, False, plan=plan)
+    assert ops.mla_read_device_errors() & 8
+
+    s = W.sparse_workload("badmeta8", 162, 2, 64, 128, [100, 70], context=512)
+    ts = G.dev_tensors(s)
+    ws = ops.mla_pack_selected_kv(ts["kcache_rec"], ts["indices"], ts["seqlens"])
+    for fmt, kv, ix in ((ops.KV_FP8_PACKED, ws, None), (ops.KV_FP8_INDEXED, ts["kcache_rec"], ts["indices"])):
+        plan = ops.DecodePlan(ts["seqlens"], s.s_q, s.h_q, fmt, num_parts=4, topk_capacity=s.topk_capacity)
+        assert int(plan.sched_meta[1, 0]) >= 0
+        plan.sched_meta[1, 3] = -1  # end block
+        ops.mla_decode(ts["q"], kv, ix, ts["seqlens"], s.scale, False, plan=plan, kv_format=fmt,
+                       topk_capacity=s.topk_capacity)
+        assert ops.mla_read_device_errors() & 8, fmt
+    assert ops.mla_read_device_errors() == 0
+
+
 # ----------------------------------------------------------------------------- HIP graph capture
 
 def test_hip_graph_replay_matches_eager():
